@@ -1,0 +1,60 @@
+"""Independent brute-force simulator for tiny traces (no sort keys).
+
+It keeps an explicit recency list of the C LRU slots, least recently used
+first.  A step takes the victims from the front of the list, skipping slots
+the step referenced; afterwards every slot the step referenced or filled moves
+to the back in ascending slot order (they all share the newest stamp, so the
+slot number breaks the tie).  This is a different formulation from the
+oracle's "sort the unreferenced slots by (last_use, slot)"; agreement of the
+two on every tiny trace pins the oracle's victim order.
+
+Resident-window rows (last R positions, ring slot C + p mod R) and padding
+(-1) follow the same readings as the oracle.  Plain Python, tiny inputs only.
+"""
+from __future__ import annotations
+
+
+class BruteStream:
+    def __init__(self, C: int, R: int):
+        self.C, self.R = C, R
+        self.recency = list(range(C))          # front = least recently used
+        self.where = {}                        # position -> slot
+        self.held = [None] * C                 # slot -> position
+
+    def resolve(self, sel, ctx):
+        for p in sel:
+            if p < -1 or p >= ctx:
+                return None
+        pos = [p for p in sel if p >= 0]
+        if len(set(pos)) != len(pos) or len(sel) > self.C:
+            return None
+        out = [None] * len(sel)
+        touched = set()
+        misses = []
+        for i, p in enumerate(sel):
+            if p == -1:
+                out[i] = -1
+            elif self.R > 0 and p >= ctx - self.R:
+                out[i] = self.C + p % self.R
+            elif p in self.where:
+                out[i] = self.where[p]
+                touched.add(self.where[p])
+            else:
+                misses.append(i)
+        candidates = [s for s in self.recency if s not in touched]
+        log = []
+        for j, i in enumerate(misses):
+            s = candidates[j]
+            old = self.held[s]
+            log.append((s, -1 if old is None else old))
+            if old is not None:
+                del self.where[old]
+            self.where[sel[i]] = s
+            self.held[s] = sel[i]
+            touched.add(s)
+            out[i] = s
+        self.recency = [s for s in self.recency if s not in touched] + sorted(touched)
+        return out, log
+
+    def slot2pos(self):
+        return [-1 if p is None else p for p in self.held]
