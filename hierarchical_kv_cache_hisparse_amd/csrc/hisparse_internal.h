@@ -1,0 +1,96 @@
+// Internal declarations shared by the host runtime and the gfx950 kernels of
+// libhisparse.  Not part of the C ABI (see include/hisparse.h).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hisparse.h"
+
+namespace hsp {
+
+// Per-stream header words (int32), see hisparse_meta_layout.
+enum HdrWord : int {
+  kHdrT = 0,        // LRU clock: number of resolves done
+  kHdrStatus = 1,   // status bits of the last resolve
+  kHdrPad = 2,      // counters of the last resolve ...
+  kHdrRes = 3,
+  kHdrHit = 4,
+  kHdrMiss = 5,
+  kHdrEvict = 6,
+  kHdrBytes = 7,
+  kHdrTotalMiss = 8,    // int64 running totals since the last reset ...
+  kHdrTotalEvict = 10,
+  kHdrTotalHit = 12,
+  kHdrWords = 16,
+};
+
+constexpr int kMaxThreads = 1024;     // resolve workgroup size ceiling
+constexpr int kMaxItems = 16;         // items per thread ceiling (C <= 16384)
+constexpr int kMaxTopK = 4096;
+constexpr int kMaxSlots = 16384;
+constexpr size_t kMaxLdsBytes = 65536;
+constexpr int kFetchThreads = 256;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte layout of the metadata buffer (mirrors hisparse_meta_layout).
+inline hisparse_meta_layout meta_layout(const hisparse_config& c) {
+  hisparse_meta_layout m{};
+  m.status = 0;
+  m.stream_base = 256;
+  m.hdr = 0;
+  m.pos2slot = 256;
+  m.slot2pos = m.pos2slot + align256(4 * (size_t)c.max_positions);
+  m.last_use = m.slot2pos + align256(4 * (size_t)c.cache_slots);
+  m.lru_order = m.last_use + align256(4 * (size_t)c.cache_slots);
+  m.evict_log = m.lru_order + align256(4 * (size_t)c.cache_slots);
+  m.miss_list = m.evict_log + align256(8 * (size_t)c.top_k);
+  m.stream_stride = m.miss_list + align256(8 * (size_t)c.top_k);
+  m.total_bytes =
+      m.stream_base + (size_t)c.num_layers * (size_t)c.num_requests * m.stream_stride;
+  return m;
+}
+
+// Launch shape of the resolve kernel: `items` entries per thread (a power of
+// two) and `threads` threads cover max(k, C) entries.
+struct ResolveShape {
+  int items;
+  int threads;
+  size_t lds_bytes;
+};
+
+// Everything a kernel needs to address one layer's streams.
+struct StreamView {
+  uint8_t* meta;          // metadata buffer base
+  uint8_t* cache;         // device cache base
+  uint8_t* const* host;   // device array [L*B] of host-history pointers
+  int64_t stream_stride;  // bytes between stream blocks
+  int64_t off_hdr, off_pos2slot, off_slot2pos, off_last_use, off_order, off_evict,
+      off_miss;
+  int64_t stream_base;
+  int64_t row_bytes;
+  int32_t B, L, C, R, k;
+  int32_t l_cap;
+  uint32_t flags;
+};
+
+ResolveShape resolve_shape(int k, int C, bool debug_validate);
+
+// Kernel launchers (hisparse_kernels.hip).  All are asynchronous on `s`.
+hipError_t launch_init(const StreamView& v, hipStream_t s, int layer, int request,
+                       bool clear_status);
+hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const int32_t* sel,
+                          const int32_t* ctx_len, int32_t* out, int32_t* sel_copy);
+hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid_x);
+hipError_t launch_prefetch_join(const StreamView& v, hipStream_t s, const int32_t* sel,
+                                const int32_t* sel_copy, const int32_t* pf_out, int32_t* out);
+hipError_t launch_load_window(const StreamView& v, hipStream_t s, int layer,
+                              const int32_t* ctx_len);
+hipError_t launch_append(const StreamView& v, hipStream_t s, int layer, const uint8_t* rows,
+                         const int32_t* pos);
+hipError_t launch_probe_host_read(hipStream_t s, const void* host, void* dev, size_t bytes,
+                                  int workgroups);
+
+}  // namespace hsp

@@ -1,0 +1,463 @@
+// Host runtime of libhisparse: the C ABI declared in include/hisparse.h.
+//
+// It validates shapes, owns the handle (events, a device copy of the host
+// history pointers, per-layer prefetch buffers) and enqueues the gfx950
+// kernels.  resolve / prefetch / append / load_window / reset never
+// synchronize, allocate or read device memory, so a caller can capture them
+// into a HIP graph ("HiSparse: Scaling Sparse-Attention Decoding with
+// Hierarchical KV Cache Management", Abstract: resolution runs inside the
+// decode graph; "Hybrid HiSparse", Timeline: the kernel is graph-capturable).
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "hisparse.h"
+#include "hisparse_internal.h"
+
+using namespace hsp;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HISPARSE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+#define HIP_TRY(call)                           \
+  do {                                          \
+    hipError_t e_ = (call);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+  } while (0)
+
+constexpr uint32_t kKnownFlags =
+    HISPARSE_NO_IO | HISPARSE_DEBUG_VALIDATE | HISPARSE_SERIALIZE_PREFETCH;
+
+int validate_config(const hisparse_config* c) {
+  if (!c) return fail(HISPARSE_ERR_INVALID_ARG, "config is NULL");
+  if (c->num_requests < 1 || c->num_layers < 1)
+    return fail(HISPARSE_ERR_INVALID_ARG, "num_requests and num_layers must be >= 1");
+  if (c->max_positions < 1 || c->max_positions >= (int64_t(1) << 31))
+    return fail(HISPARSE_ERR_INVALID_ARG, "max_positions must be in [1, 2^31)");
+  if (c->row_bytes <= 0 || c->row_bytes % 16 != 0)
+    return fail(HISPARSE_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 16");
+  if (c->top_k < 1) return fail(HISPARSE_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (c->cache_slots < c->top_k)
+    return fail(HISPARSE_ERR_INVALID_ARG, "cache_slots (%d) must be >= top_k (%d)",
+                c->cache_slots, c->top_k);
+  if (c->resident_window < 0)
+    return fail(HISPARSE_ERR_INVALID_ARG, "resident_window must be >= 0");
+  if (c->flags & ~kKnownFlags) return fail(HISPARSE_ERR_INVALID_ARG, "unknown flags 0x%x", c->flags);
+  if (c->top_k > kMaxTopK)
+    return fail(HISPARSE_ERR_UNSUPPORTED, "top_k %d exceeds %d", c->top_k, kMaxTopK);
+  if (c->cache_slots > kMaxSlots)
+    return fail(HISPARSE_ERR_UNSUPPORTED, "cache_slots %d exceeds %d", c->cache_slots, kMaxSlots);
+  if ((int64_t)c->cache_slots + c->resident_window >= (int64_t(1) << 31))
+    return fail(HISPARSE_ERR_INVALID_ARG, "cache_slots + resident_window too large");
+  // (C+R) * row_bytes must fit the 32-bit byte counters of one slot row set
+  const double per_stream = (double)(c->cache_slots + c->resident_window) * c->row_bytes;
+  if (per_stream * c->num_layers * c->num_requests > 9.0e18)
+    return fail(HISPARSE_ERR_INVALID_ARG, "cache size overflows");
+  if ((int64_t)c->top_k * c->row_bytes >= (int64_t(1) << 31))
+    return fail(HISPARSE_ERR_UNSUPPORTED, "top_k * row_bytes must be < 2^31");
+  const ResolveShape sh =
+      resolve_shape(c->top_k, c->cache_slots, (c->flags & HISPARSE_DEBUG_VALIDATE) != 0);
+  if (sh.items == 0 || sh.lds_bytes > kMaxLdsBytes)
+    return fail(HISPARSE_ERR_UNSUPPORTED,
+                "C=%d, k=%d need %zu bytes of LDS per workgroup (limit %zu)", c->cache_slots,
+                c->top_k, sh.lds_bytes, kMaxLdsBytes);
+  return HISPARSE_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  return atoi(s);
+}
+
+struct TimedCall {
+  hipEvent_t e0, e1, e2;  // before resolve, after resolve, after fetch
+  bool fetched;
+};
+
+}  // namespace
+
+struct hisparse {
+  hisparse_config cfg;
+  hisparse_meta_layout lay;
+  int device = 0;
+  StreamView view{};
+  uint8_t** d_host = nullptr;    // [L*B] host-history pointers, device copy
+  int32_t* pf_out = nullptr;     // [L][B][k] prefetched slot maps
+  int32_t* pf_sel = nullptr;     // [L][B][k] prefetched selections
+  std::vector<uint8_t> pending;  // per layer: a prefetch waits to be joined
+  std::vector<hipEvent_t> ev_fork, ev_done;
+  int fetch_grid_x = 1;
+  // timing of eager calls
+  bool timing = false;
+  std::vector<TimedCall> pool;
+  size_t pool_used = 0;
+  hisparse_timing totals{};
+};
+
+namespace {
+
+int fold_timing(hisparse* h) {
+  for (size_t i = 0; i < h->pool_used; ++i) {
+    TimedCall& c = h->pool[i];
+    HIP_TRY(hipEventSynchronize(c.e2));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, c.e0, c.e1));
+    h->totals.resolve_ms += ms;
+    h->totals.resolve_launches += 1;
+    if (c.fetched) {
+      HIP_TRY(hipEventElapsedTime(&ms, c.e1, c.e2));
+      h->totals.fetch_ms += ms;
+      h->totals.fetch_launches += 1;
+    }
+  }
+  h->pool_used = 0;
+  return HISPARSE_OK;
+}
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+// resolve kernel (+ fetch unless NO_IO) of one layer on one stream
+int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_t* ctx_len,
+                    int layer, int32_t* out, int32_t* sel_copy) {
+  const bool io = !(h->cfg.flags & HISPARSE_NO_IO);
+  TimedCall* tc = nullptr;
+  if (h->timing && !capturing(s)) {
+    if (h->pool_used == h->pool.size()) {
+      int rc = fold_timing(h);
+      if (rc) return rc;
+    }
+    tc = &h->pool[h->pool_used++];
+    tc->fetched = io;
+    HIP_TRY(hipEventRecord(tc->e0, s));
+  }
+  HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy));
+  if (tc) HIP_TRY(hipEventRecord(tc->e1, s));
+  if (io) HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
+  if (tc) HIP_TRY(hipEventRecord(tc->e2, s));
+  return HISPARSE_OK;
+}
+
+void release(hisparse* h) {
+  if (!h) return;
+  for (auto e : h->ev_fork) if (e) (void)hipEventDestroy(e);
+  for (auto e : h->ev_done) if (e) (void)hipEventDestroy(e);
+  for (auto& c : h->pool) {
+    (void)hipEventDestroy(c.e0);
+    (void)hipEventDestroy(c.e1);
+    (void)hipEventDestroy(c.e2);
+  }
+  if (h->d_host) (void)hipFree(h->d_host);
+  if (h->pf_out) (void)hipFree(h->pf_out);
+  if (h->pf_sel) (void)hipFree(h->pf_sel);
+  delete h;
+}
+
+int check_device_buffer(const void* p, const char* name) {
+  if (!p) return fail(HISPARSE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 256 != 0)
+    return fail(HISPARSE_ERR_INVALID_ARG, "%s must be 256-byte aligned", name);
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess || attr.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return fail(HISPARSE_ERR_INVALID_ARG, "%s is not device memory", name);
+  }
+  return HISPARSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hisparse_workspace_bytes(const hisparse_config* cfg, size_t* cache_bytes, size_t* meta_bytes) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (cache_bytes)
+    *cache_bytes = (size_t)cfg->num_layers * cfg->num_requests *
+                   ((size_t)cfg->cache_slots + cfg->resident_window) * cfg->row_bytes;
+  if (meta_bytes) *meta_bytes = meta_layout(*cfg).total_bytes;
+  return HISPARSE_OK;
+}
+
+int hisparse_meta_layout_of(const hisparse_config* cfg, hisparse_meta_layout* out) {
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(HISPARSE_ERR_INVALID_ARG, "out is NULL");
+  *out = meta_layout(*cfg);
+  return HISPARSE_OK;
+}
+
+int hisparse_host_alloc(size_t bytes, uint32_t flags, void** host_ptr) {
+  if (!host_ptr) return fail(HISPARSE_ERR_INVALID_ARG, "host_ptr is NULL");
+  *host_ptr = nullptr;
+  if (bytes == 0) return fail(HISPARSE_ERR_INVALID_ARG, "bytes is 0");
+  if (flags & ~HISPARSE_HOST_NONCOHERENT)
+    return fail(HISPARSE_ERR_INVALID_ARG, "unknown host flags 0x%x", flags);
+  unsigned hf = hipHostMallocMapped | hipHostMallocPortable |
+                ((flags & HISPARSE_HOST_NONCOHERENT) ? hipHostMallocNonCoherent
+                                                     : hipHostMallocCoherent);
+  hipError_t e = hipHostMalloc(host_ptr, bytes, hf);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    *host_ptr = nullptr;
+    return fail(HISPARSE_ERR_OOM, "hipHostMalloc of %zu bytes failed: %s", bytes,
+                hipGetErrorString(e));
+  }
+  return HISPARSE_OK;
+}
+
+int hisparse_host_free(void* host_ptr) {
+  if (!host_ptr) return HISPARSE_OK;
+  HIP_TRY(hipHostFree(host_ptr));
+  return HISPARSE_OK;
+}
+
+int hisparse_create(const hisparse_config* cfg, void* const* host_rows, void* device_cache,
+                    void* device_meta, hisparse_t* out) {
+  if (!out) return fail(HISPARSE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!host_rows) return fail(HISPARSE_ERR_INVALID_ARG, "host_rows is NULL");
+  if ((rc = check_device_buffer(device_cache, "device_cache"))) return rc;
+  if ((rc = check_device_buffer(device_meta, "device_meta"))) return rc;
+  const int L = cfg->num_layers, B = cfg->num_requests;
+  std::vector<uint8_t*> dev_host((size_t)L * B);
+  for (int i = 0; i < L * B; ++i) {
+    if (!host_rows[i]) return fail(HISPARSE_ERR_INVALID_ARG, "host_rows[%d] is NULL", i);
+    void* dp = nullptr;
+    if (hipHostGetDevicePointer(&dp, host_rows[i], 0) != hipSuccess || !dp) {
+      (void)hipGetLastError();
+      return fail(HISPARSE_ERR_INVALID_ARG,
+                  "host_rows[%d] is not pinned, device-mapped host memory", i);
+    }
+    dev_host[i] = static_cast<uint8_t*>(dp);
+  }
+
+  hisparse* h = new (std::nothrow) hisparse();
+  if (!h) return fail(HISPARSE_ERR_OOM, "handle allocation failed");
+  h->cfg = *cfg;
+  h->lay = meta_layout(*cfg);
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) { release(h); return hip_fail(e, "hipGetDevice"); }
+  h->pending.assign(L, 0);
+  h->ev_fork.assign(L, nullptr);
+  h->ev_done.assign(L, nullptr);
+  const size_t map_bytes = sizeof(int32_t) * (size_t)L * B * cfg->top_k;
+  if (hipMalloc(reinterpret_cast<void**>(&h->d_host), sizeof(uint8_t*) * L * B) != hipSuccess ||
+      hipMalloc(reinterpret_cast<void**>(&h->pf_out), map_bytes) != hipSuccess ||
+      hipMalloc(reinterpret_cast<void**>(&h->pf_sel), map_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    release(h);
+    return fail(HISPARSE_ERR_OOM, "device allocation of handle buffers failed");
+  }
+  for (int l = 0; l < L; ++l) {
+    if (hipEventCreateWithFlags(&h->ev_fork[l], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->ev_done[l], hipEventDisableTiming) != hipSuccess) {
+      release(h);
+      return fail(HISPARSE_ERR_HIP, "event creation failed");
+    }
+  }
+  e = hipMemcpy(h->d_host, dev_host.data(), sizeof(uint8_t*) * L * B, hipMemcpyHostToDevice);
+  if (e != hipSuccess) { release(h); return hip_fail(e, "hipMemcpy(host pointers)"); }
+
+  StreamView& v = h->view;
+  v.meta = static_cast<uint8_t*>(device_meta);
+  v.cache = static_cast<uint8_t*>(device_cache);
+  v.host = h->d_host;
+  v.stream_stride = (int64_t)h->lay.stream_stride;
+  v.stream_base = (int64_t)h->lay.stream_base;
+  v.off_hdr = (int64_t)h->lay.hdr;
+  v.off_pos2slot = (int64_t)h->lay.pos2slot;
+  v.off_slot2pos = (int64_t)h->lay.slot2pos;
+  v.off_last_use = (int64_t)h->lay.last_use;
+  v.off_order = (int64_t)h->lay.lru_order;
+  v.off_evict = (int64_t)h->lay.evict_log;
+  v.off_miss = (int64_t)h->lay.miss_list;
+  v.row_bytes = cfg->row_bytes;
+  v.B = B;
+  v.L = L;
+  v.C = cfg->cache_slots;
+  v.R = cfg->resident_window;
+  v.k = cfg->top_k;
+  v.l_cap = (int32_t)cfg->max_positions;
+  v.flags = cfg->flags;
+
+  // Fetch fan-out: about `wgs` workgroups in total, split over the requests.
+  const int wgs = env_int("HISPARSE_FETCH_WORKGROUPS", 1024);
+  h->fetch_grid_x = wgs / B > 1 ? wgs / B : 1;
+
+  e = launch_init(v, nullptr, -1, -1, true);
+  if (e == hipSuccess) e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) { release(h); return hip_fail(e, "metadata initialisation"); }
+  *out = h;
+  return HISPARSE_OK;
+}
+
+int hisparse_destroy(hisparse_t h) {
+  if (!h) return HISPARSE_OK;
+  (void)hipDeviceSynchronize();
+  release(h);
+  return HISPARSE_OK;
+}
+
+int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel, const int32_t* ctx_len,
+                     int32_t layer, int32_t* out_slot) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  if (!sel || !ctx_len || !out_slot)
+    return fail(HISPARSE_ERR_INVALID_ARG, "sel, ctx_len and out_slot must not be NULL");
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
+  if (h->pending[layer]) {
+    // join the prefetch: wait for it, then hand over its slot map
+    HIP_TRY(hipStreamWaitEvent(stream, h->ev_done[layer], 0));
+    const size_t off = (size_t)layer * h->cfg.num_requests * h->cfg.top_k;
+    HIP_TRY(launch_prefetch_join(h->view, stream, sel, h->pf_sel + off, h->pf_out + off,
+                                 out_slot));
+    h->pending[layer] = 0;
+    return HISPARSE_OK;
+  }
+  return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr);
+}
+
+int hisparse_prefetch(hisparse_t h, hipStream_t main_stream, hipStream_t side_stream,
+                      const int32_t* sel, const int32_t* ctx_len, int32_t layer) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  if (!sel || !ctx_len) return fail(HISPARSE_ERR_INVALID_ARG, "sel and ctx_len must not be NULL");
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
+  if (h->pending[layer])
+    return fail(HISPARSE_ERR_STATE, "layer %d already has a pending prefetch", layer);
+  const bool serial = (h->cfg.flags & HISPARSE_SERIALIZE_PREFETCH) || side_stream == main_stream;
+  hipStream_t s = serial ? main_stream : side_stream;
+  if (!serial) {
+    HIP_TRY(hipEventRecord(h->ev_fork[layer], main_stream));
+    HIP_TRY(hipStreamWaitEvent(side_stream, h->ev_fork[layer], 0));
+  }
+  const size_t off = (size_t)layer * h->cfg.num_requests * h->cfg.top_k;
+  int rc = enqueue_resolve(h, s, sel, ctx_len, layer, h->pf_out + off, h->pf_sel + off);
+  if (rc) return rc;
+  HIP_TRY(hipEventRecord(h->ev_done[layer], s));
+  h->pending[layer] = 1;
+  return HISPARSE_OK;
+}
+
+int hisparse_load_window(hisparse_t h, hipStream_t stream, int32_t layer, const int32_t* ctx_len) {
+  if (!h || !ctx_len) return fail(HISPARSE_ERR_INVALID_ARG, "handle and ctx_len must not be NULL");
+  if (layer < -1 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  HIP_TRY(launch_load_window(h->view, stream, layer, ctx_len));
+  return HISPARSE_OK;
+}
+
+int hisparse_append(hisparse_t h, hipStream_t stream, int32_t layer, const void* rows,
+                    const int32_t* pos) {
+  if (!h || !rows || !pos) return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (reinterpret_cast<uintptr_t>(rows) % 16 != 0)
+    return fail(HISPARSE_ERR_INVALID_ARG, "rows must be 16-byte aligned");
+  HIP_TRY(launch_append(h->view, stream, layer, static_cast<const uint8_t*>(rows), pos));
+  return HISPARSE_OK;
+}
+
+int hisparse_reset(hisparse_t h, hipStream_t stream, int32_t layer, int32_t request) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  if (layer < -1 || layer >= h->cfg.num_layers || request < -1 ||
+      request >= h->cfg.num_requests)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer/request out of range");
+  for (int l = 0; l < h->cfg.num_layers; ++l)
+    if ((layer < 0 || l == layer) && h->pending[l])
+      return fail(HISPARSE_ERR_STATE, "layer %d has a pending prefetch", l);
+  HIP_TRY(launch_init(h->view, stream, layer, request, false));
+  return HISPARSE_OK;
+}
+
+int hisparse_get_status(hisparse_t h, uint32_t* status, int clear) {
+  if (!h || !status) return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(status, h->view.meta + h->lay.status, sizeof(uint32_t),
+                    hipMemcpyDeviceToHost));
+  if (clear) {
+    const uint32_t zero = 0;
+    HIP_TRY(hipMemcpy(h->view.meta + h->lay.status, &zero, sizeof(uint32_t),
+                      hipMemcpyHostToDevice));
+  }
+  return HISPARSE_OK;
+}
+
+int hisparse_set_timing(hisparse_t h, int enable) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  if (enable && h->pool.empty()) {
+    const size_t n = 1024;
+    h->pool.resize(n);
+    for (auto& c : h->pool) {
+      if (hipEventCreate(&c.e0) != hipSuccess || hipEventCreate(&c.e1) != hipSuccess ||
+          hipEventCreate(&c.e2) != hipSuccess)
+        return fail(HISPARSE_ERR_HIP, "timing event creation failed");
+    }
+  }
+  h->timing = enable != 0;
+  h->pool_used = 0;
+  h->totals = hisparse_timing{};
+  return HISPARSE_OK;
+}
+
+int hisparse_get_timing(hisparse_t h, hisparse_timing* out) {
+  if (!h || !out) return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  int rc = fold_timing(h);
+  if (rc) return rc;
+  *out = h->totals;
+  return HISPARSE_OK;
+}
+
+int hisparse_probe_host_read(hipStream_t stream, const void* host, void* device, size_t bytes,
+                             int32_t workgroups) {
+  if (!host || !device || bytes == 0 || bytes % 16 != 0 || workgroups < 1)
+    return fail(HISPARSE_ERR_INVALID_ARG, "bad probe arguments");
+  if (reinterpret_cast<uintptr_t>(host) % 16 || reinterpret_cast<uintptr_t>(device) % 16)
+    return fail(HISPARSE_ERR_INVALID_ARG, "probe buffers must be 16-byte aligned");
+  HIP_TRY(launch_probe_host_read(stream, host, device, bytes, workgroups));
+  return HISPARSE_OK;
+}
+
+const char* hisparse_strerror(int code) {
+  switch (code) {
+    case HISPARSE_OK: return "success";
+    case HISPARSE_ERR_INVALID_ARG: return "invalid argument";
+    case HISPARSE_ERR_OOM: return "out of memory";
+    case HISPARSE_ERR_HIP: return "HIP runtime error";
+    case HISPARSE_ERR_STATE: return "call out of order";
+    case HISPARSE_ERR_UNSUPPORTED: return "unsupported shape";
+    default: return "unknown error code";
+  }
+}
+
+const char* hisparse_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+"""The C-ABI library loads and exports every symbol include/hisparse.h
+declares, and its host-only logic (shape validation, workspace sizes, the
+metadata layout, error strings) behaves as documented (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hierarchical_kv_cache_hisparse_amd import binding as hb
+from workload import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hisparse.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hisparse_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("hisparse_create", "hisparse_resolve", "hisparse_prefetch", "hisparse_destroy"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hb.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_has_the_same_names():
+    missing = [n for n in declared_functions() if not hasattr(hb, n)]
+    assert not missing, missing
+
+
+def _cfg(w, flags=0):
+    return hb.make_config(w.B, w.layers, w.l_cap, w.row_bytes, w.C, w.R, w.k, flags)
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_workspace_sizes_of_the_workloads(cfg_id):
+    w = CONFIGS[cfg_id]
+    cache, meta = hb.hisparse_workspace_bytes(_cfg(w))
+    assert cache == w.layers * w.B * (w.C + w.R) * w.row_bytes
+    lay = hb.hisparse_meta_layout_of(_cfg(w))
+    assert lay.total_bytes == meta
+    offs = [lay.hdr, lay.pos2slot, lay.slot2pos, lay.last_use, lay.lru_order, lay.evict_log,
+            lay.miss_list]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.slot2pos - lay.pos2slot >= 4 * w.l_cap
+    assert lay.stream_stride - lay.miss_list >= 8 * w.k
+    assert lay.stream_base >= 4 and lay.stream_base % 256 == 0
+    assert meta == lay.stream_base + w.layers * w.B * lay.stream_stride
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_requests", 0, hb.HISPARSE_ERR_INVALID_ARG),
+    ("num_layers", 0, hb.HISPARSE_ERR_INVALID_ARG),
+    ("max_positions", 0, hb.HISPARSE_ERR_INVALID_ARG),
+    ("max_positions", 1 << 31, hb.HISPARSE_ERR_INVALID_ARG),
+    ("row_bytes", 1000, hb.HISPARSE_ERR_INVALID_ARG),
+    ("row_bytes", 0, hb.HISPARSE_ERR_INVALID_ARG),
+    ("cache_slots", 100, hb.HISPARSE_ERR_INVALID_ARG),      # C < k
+    ("resident_window", -1, hb.HISPARSE_ERR_INVALID_ARG),
+    ("top_k", 0, hb.HISPARSE_ERR_INVALID_ARG),
+    ("top_k", 8192, hb.HISPARSE_ERR_INVALID_ARG),          # > C
+    ("flags", 0x100, hb.HISPARSE_ERR_INVALID_ARG),
+    ("cache_slots", 20000, hb.HISPARSE_ERR_UNSUPPORTED),
+])
+def test_invalid_configs_are_rejected_on_the_host(field, value, code):
+    cfg = _cfg(CONFIGS[2])
+    setattr(cfg, field, value)
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_workspace_bytes(cfg)
+    assert e.value.code == code
+    assert hb.hisparse_last_error()
+
+
+def test_lds_limit_is_enforced():
+    cfg = hb.make_config(1, 1, 1 << 20, 1152, 16384, 0, 4096, hb.HISPARSE_DEBUG_VALIDATE)
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_workspace_bytes(cfg)
+    assert e.value.code == hb.HISPARSE_ERR_UNSUPPORTED
+
+
+def test_error_strings():
+    assert hb.hisparse_strerror(0) == "success"
+    assert "invalid" in hb.hisparse_strerror(hb.HISPARSE_ERR_INVALID_ARG)
+    assert hb.hisparse_strerror(-99) == "unknown error code"
+
+
+def test_create_rejects_null_and_host_pointers_without_touching_them():
+    cfg = _cfg(CONFIGS[1])
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_create(cfg, [None], 0, 0)
+    assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+    buf = (ctypes.c_uint8 * 4096)()
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_create(cfg, [ctypes.addressof(buf)], ctypes.addressof(buf),
+                           ctypes.addressof(buf))
+    assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+
+
+def test_host_alloc_rejects_bad_arguments():
+    with pytest.raises(hb.HisparseError):
+        hb.hisparse_host_alloc(0)
+    with pytest.raises(hb.HisparseError):
+        hb.hisparse_host_alloc(4096, 0x80)
