@@ -84,6 +84,13 @@ def library():
             raise ImportError(
                 f"{LIB_PATH} not found: build it with `python -m "
                 "hierarchical_kv_cache_hisparse_amd.build` (or __graft_entry__.build())")
+        # One HIP runtime per process: PyTorch ships its own libamdhip64.so.7.
+        # Loading torch first makes the library bind to that runtime by soname
+        # instead of pulling in a second one (which leaves torch without a GPU).
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(LIB_PATH)
         P, I32, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         sig = {

@@ -30,7 +30,8 @@ constexpr int kMaxThreads = 1024;     // resolve workgroup size ceiling
 constexpr int kMaxItems = 16;         // items per thread ceiling (C <= 16384)
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxSlots = 16384;
-constexpr size_t kMaxLdsBytes = 65536;
+constexpr int kMaxRequests = 32768;   // the fetch kernel keeps B+1 prefixes in LDS
+constexpr size_t kMaxLdsBytes = 163840;   // gfx950: 160 KiB of LDS per workgroup
 constexpr int kFetchThreads = 256;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -74,7 +75,14 @@ struct StreamView {
   int32_t B, L, C, R, k;
   int32_t l_cap;
   uint32_t flags;
+  uint32_t r_magic;    // floor(2^32 / R) (2^32 - 1 for R <= 1): fast p mod R
+  uint32_t cpr_magic;  // the same for row_bytes / 16 (16-byte chunks per row)
+  int32_t fuse_fetch;  // resolve workgroups copy their own misses
 };
+
+inline uint32_t div_magic(uint32_t d) {
+  return d <= 1 ? 0xFFFFFFFFu : (uint32_t)((uint64_t(1) << 32) / d);
+}
 
 ResolveShape resolve_shape(int k, int C, bool debug_validate);
 

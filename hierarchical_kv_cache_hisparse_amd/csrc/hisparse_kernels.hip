@@ -40,12 +40,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 enum Cls : int { kNone = 0, kPad = 1, kRes = 2, kHit = 3, kMiss = 4, kBad = 5 };
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 struct StreamPtrs {
   int32_t* hdr;
   int32_t* pos2slot;
@@ -73,6 +67,50 @@ __device__ __forceinline__ uint32_t* status_word(const StreamView& v) {
   return (uint32_t*)v.meta;
 }
 
+// Workgroup barrier for LDS only.  No wave of the resolve kernel reads global
+// memory that another wave of it wrote, so a barrier never has to wait for
+// outstanding global stores (HIP's __syncthreads would: it fences global
+// memory too, which costs a store round trip per barrier).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then the row totals are carried with
+// the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2
+// and 3).  Six VALU operations, no LDS traffic.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Quotient and remainder of p < 2^31 by d >= 1, given magic = floor(2^32/d)
+// (2^32 - 1 for d = 1): the estimate umulhi(p, magic) is q or q - 1.
+__device__ __forceinline__ uint32_t fast_div(uint32_t p, uint32_t d, uint32_t magic,
+                                             uint32_t* rem) {
+  uint32_t q = __umulhi(p, magic);
+  uint32_t r = p - q * d;
+  if (r >= d) {
+    r -= d;
+    ++q;
+  }
+  *rem = r;
+  return q;
+}
+
+__device__ __forceinline__ uint32_t fast_mod(uint32_t p, uint32_t d, uint32_t magic) {
+  uint32_t r;
+  fast_div(p, d, magic, &r);
+  return r;
+}
+
 // Ordered compaction, part 1: per round r, the lane's rank among the flagged
 // lanes of its wave, and (lane 0) the wave's count into cnt[r*W + wave].
 template <int IPT>
@@ -87,22 +125,28 @@ __device__ __forceinline__ void ballot_counts(const bool (&flag)[IPT], int* cnt,
   }
 }
 
-// Ordered compaction, part 2 (after a barrier): off[r] = number of flagged
-// items before (round r, this wave); returns the total.  Every wave computes
-// its own offsets, so no extra barrier is needed.
-template <int IPT>
-__device__ __forceinline__ int wave_offsets(const int* cnt, int W, int wave, int lane,
+// Ordered compaction, part 2: one wave-wide scan over the IPT*W counts
+// (count(e) for e = r*W + w, in that order); off[r] = number of flagged items
+// before (round r, this wave).  Returns the total.  Every wave computes its
+// own offsets, so no barrier is needed after it.
+template <int IPT, typename CountFn>
+__device__ __forceinline__ int scan_offsets(CountFn count, int W, int wave, int lane,
                                             int (&off)[IPT]) {
+  const int n = IPT * W;
+  int carry = 0;
+  for (int c = 0; c < n; c += 64) {
+    const int e = c + lane;
+    const int v = e < n ? count(e) : 0;
+    const int incl = wave_inclusive_scan(v);
+    const int excl = incl - v + carry;
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
-    const int lim = r * W + wave;
-    int s = 0;
-    for (int e = lane; e < lim; e += 64) s += cnt[e];
-    off[r] = wave_sum(s);
+    for (int r = 0; r < IPT; ++r) {
+      const int idx = r * W + wave;  // wave-uniform
+      if (idx >= c && idx < c + 64) off[r] = __builtin_amdgcn_readlane(excl, idx - c);
+    }
+    carry += __builtin_amdgcn_readlane(incl, 63);
   }
-  int s = 0;
-  for (int e = lane; e < IPT * W; e += 64) s += cnt[e];
-  return wave_sum(s);
+  return carry;
 }
 
 __device__ __forceinline__ bool test_bit(const uint32_t* bm, int s) {
@@ -111,6 +155,17 @@ __device__ __forceinline__ bool test_bit(const uint32_t* bm, int s) {
 
 // ---------------------------------------------------------------------------
 // Resolve: one workgroup per stream (request b of `layer`).
+//
+// The stream's work runs on one CU, so the kernel is bound by how many
+// scattered (one cache line per lane) global accesses it issues.  Only the
+// position->slot gathers and the two position->slot updates per miss are
+// scattered; last_use and slot2pos are rewritten densely in slot order.
+//
+// Barriers (LDS only): Z after clearing LDS; 1 after classification (hit
+// bitmap, class counters, miss counts, error bits); 2 after the misses are
+// staged and the unreferenced slots counted; 3 after the victims are taken.
+// No global write happens before barrier 1, so a rejected row leaves the
+// stream untouched.
 // ---------------------------------------------------------------------------
 template <int IPT>
 __global__ void __launch_bounds__(kMaxThreads)
@@ -123,32 +178,27 @@ __global__ void __launch_bounds__(kMaxThreads)
   const int BD = blockDim.x;
   const int W = BD >> 6;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int C = v.C, R = v.R, k = v.k;
   const bool debug = (v.flags & HISPARSE_DEBUG_VALIDATE) != 0;
   const StreamPtrs st = stream_ptrs(v, layer, b);
   const int32_t* sel = sel_all + (int64_t)b * k;
   int32_t* out = out_all + (int64_t)b * k;
 
-  // LDS: [bitmap C bits][slot2pos C][victims k][3 x count tables][misc 8][hash]
+  // LDS: [bitmap C bits][slot2pos C][miss pos k][miss idx k][cntA][cntB][misc 8][hash]
   const int nbm = (C + 31) >> 5;
   uint32_t* bitmap = (uint32_t*)lds;
   int* s2p = lds + nbm;
-  int* victim = s2p + C;
-  int* cntA = victim + k;
+  int* missp = s2p + C;
+  int* missi = missp + k;
+  int* cntA = missi + k;
   int* cntB = cntA + IPT * W;
-  int* cntC = cntB + IPT * W;
-  int* misc = cntC + IPT * W;  // 0 status, 1 pad, 2 res, 3 hit, 4 evict
+  int* misc = cntB + IPT * W;  // 0 error bits, 1 pad, 2 res, 3 hit, 4 evictions
   int* hash = misc + 8;
+  const int H = debug ? (2 << (31 - __clz(k))) : 0;  // power of two > k
 
-  // ---- Phase A: independent loads, then the position->slot gathers -------
-  const int32_t ctx = ctx_len[b];
-  const int32_t t = st.hdr[kHdrT] + 1;  // one clock tick per resolve
-  const bool ctx_ok = ctx >= 0 && ctx <= v.l_cap;
-  if (tid < 8) misc[tid] = 0;
-  for (int w = tid; w < nbm; w += BD) bitmap[w] = 0;
-
-  int32_t p[IPT], o[IPT], slot[IPT];
+  // ---- Phase A: independent loads; clear LDS ------------------------------
+  int32_t p[IPT], o[IPT], q2[IPT], slot[IPT];
   int cls[IPT];
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
@@ -159,13 +209,21 @@ __global__ void __launch_bounds__(kMaxThreads)
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
     const int x = r * BD + tid;
-    if (x < C) {
-      o[r] = st.order[x];
-      s2p[x] = st.slot2pos[x];
-    } else {
-      o[r] = 0;
-    }
+    o[r] = (x < C) ? st.order[x] : 0;
+    q2[r] = (x < C) ? st.slot2pos[x] : -1;
   }
+  const int32_t ctx = ctx_len[b];
+  const int32_t t = st.hdr[kHdrT] + 1;  // one clock tick per resolve
+  const int64_t tot_miss = *reinterpret_cast<const int64_t*>(st.hdr + kHdrTotalMiss);
+  const int64_t tot_evict = *reinterpret_cast<const int64_t*>(st.hdr + kHdrTotalEvict);
+  const int64_t tot_hit = *reinterpret_cast<const int64_t*>(st.hdr + kHdrTotalHit);
+  const bool ctx_ok = ctx >= 0 && ctx <= v.l_cap;
+  for (int w = tid; w < nbm; w += BD) bitmap[w] = 0;
+  for (int w = tid; w < H; w += BD) hash[w] = -1;
+  if (tid < 8) misc[tid] = 0;
+  lds_barrier();  // Z: LDS cleared (global loads stay in flight)
+
+  // ---- classify; the position->slot gathers -------------------------------
   uint32_t bad = ctx_ok ? 0u : (uint32_t)HISPARSE_STATUS_CTX_RANGE;
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
@@ -185,10 +243,12 @@ __global__ void __launch_bounds__(kMaxThreads)
       slot[r] = st.pos2slot[q];
     }
   }
+#pragma unroll
+  for (int r = 0; r < IPT; ++r) {
+    const int x = r * BD + tid;
+    if (x < C) s2p[x] = q2[r];
+  }
   if (debug) {  // repeated positions: LDS open-addressing set of size H
-    const int H = 2 << (31 - __clz(k));  // power of two > k... >= 2k
-    for (int w = tid; w < H; w += BD) hash[w] = -1;
-    __syncthreads();
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
       if (cls[r] == kNone || p[r] < 0) continue;
@@ -204,11 +264,32 @@ __global__ void __launch_bounds__(kMaxThreads)
       }
     }
   }
-  if (__syncthreads_or(bad != 0u)) {
+  bool flag[IPT];
+  int pre[IPT], off[IPT];
+  int npad = 0, nres = 0, nhit = 0;
+#pragma unroll
+  for (int r = 0; r < IPT; ++r) {
+    if (cls[r] == kMiss && slot[r] >= 0) {
+      cls[r] = kHit;
+      atomicOr(&bitmap[slot[r] >> 5], 1u << (slot[r] & 31));
+    }
+    npad += __popcll(__ballot(cls[r] == kPad));
+    nres += __popcll(__ballot(cls[r] == kRes));
+    nhit += __popcll(__ballot(cls[r] == kHit));
+    flag[r] = cls[r] == kMiss;
+  }
+  ballot_counts<IPT>(flag, cntA, W, wave, lane, pre);
+  if (bad) atomicOr((uint32_t*)&misc[0], bad);
+  if (lane == 0) {
+    if (npad) atomicAdd(&misc[1], npad);
+    if (nres) atomicAdd(&misc[2], nres);
+    if (nhit) atomicAdd(&misc[3], nhit);
+  }
+  lds_barrier();  // 1: hit bitmap, class counters, miss counts, error bits
+
+  uint32_t err = (uint32_t)misc[0];
+  if (err) {
     // Rejected row: leave the stream untouched, serve -1 everywhere.
-    if (bad) atomicOr((uint32_t*)&misc[0], bad);
-    __syncthreads();
-    uint32_t err = (uint32_t)misc[0];
     if (err & (HISPARSE_STATUS_SEL_RANGE | HISPARSE_STATUS_CTX_RANGE))
       err &= ~(uint32_t)HISPARSE_STATUS_SEL_DUP;
 #pragma unroll
@@ -226,158 +307,195 @@ __global__ void __launch_bounds__(kMaxThreads)
     }
     return;
   }
+  const int n_hit = misc[3];
 
-  // ---- Phase B: serve padding, resident rows and hits; rank the misses -----
+  // ---- serve padding, resident rows and hits; stage the misses -------------
+  const int M = scan_offsets<IPT>([&](int e) { return cntA[e]; }, W, wave, lane, off);
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
     const int i = r * BD + tid;
-    if (cls[r] == kMiss && slot[r] >= 0) cls[r] = kHit;
-    if (cls[r] == kPad) {
+    if (cls[r] == kMiss) {  // j-th miss in ascending selection index
+      const int j = off[r] + pre[r];
+      missp[j] = p[r];
+      missi[j] = i;
+    } else if (cls[r] == kPad) {
       out[i] = -1;
     } else if (cls[r] == kRes) {
-      out[i] = C + p[r] % R;
+      out[i] = C + (int)fast_mod((uint32_t)p[r], (uint32_t)R, v.r_magic);
     } else if (cls[r] == kHit) {
-      const int s = slot[r];
-      out[i] = s;
-      st.last_use[s] = t;
-      atomicOr(&bitmap[s >> 5], 1u << (s & 31));
+      out[i] = slot[r];
     }
     if (sel_copy && cls[r] != kNone) sel_copy[(int64_t)b * k + i] = p[r];
   }
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
-    const int np = __popcll(__ballot(cls[r] == kPad));
-    const int nr = __popcll(__ballot(cls[r] == kRes));
-    const int nh = __popcll(__ballot(cls[r] == kHit));
-    if (lane == 0) {
-      if (np) atomicAdd(&misc[1], np);
-      if (nr) atomicAdd(&misc[2], nr);
-      if (nh) atomicAdd(&misc[3], nh);
-    }
-  }
-  bool flag[IPT];
-  int pre[IPT], off[IPT], jm[IPT];
-#pragma unroll
-  for (int r = 0; r < IPT; ++r) flag[r] = cls[r] == kMiss;
-  ballot_counts<IPT>(flag, cntA, W, wave, lane, pre);
-  __syncthreads();  // hits marked, miss counts and class counters complete
-  const int M = wave_offsets<IPT>(cntA, W, wave, lane, off);
-  const int n_hit = misc[3];
-#pragma unroll
-  for (int r = 0; r < IPT; ++r) jm[r] = off[r] + pre[r];  // miss index j (ascending i)
-
-  // ---- Phase C: victims = first M unreferenced slots in LRU order ----------
-#pragma unroll
-  for (int r = 0; r < IPT; ++r) {
     const int x = r * BD + tid;
-    flag[r] = (x < C) && !test_bit(bitmap, o[r]);
+    flag[r] = (x < C) && !test_bit(bitmap, o[r]);  // unreferenced, in LRU order
   }
   ballot_counts<IPT>(flag, cntB, W, wave, lane, pre);
-  __syncthreads();
-  wave_offsets<IPT>(cntB, W, wave, lane, off);
+  lds_barrier();  // 2: misses staged, unreferenced-slot counts
+
+  // ---- victims = first M unreferenced slots in LRU order; the j-th miss ----
+  // takes the j-th victim.  The victim's owner thread applies the whole miss.
+  scan_offsets<IPT>([&](int e) { return cntB[e]; }, W, wave, lane, off);
+  int nev = 0;
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
     if (!flag[r]) continue;
     const int u = off[r] + pre[r];
+    const int s = o[r];
     if (u < M) {
-      victim[u] = o[r];
-      atomicOr(&bitmap[o[r] >> 5], 1u << (o[r] & 31));
+      const int pos = missp[u];
+      const int q = s2p[s];
+      reinterpret_cast<int2*>(st.evict)[u] = make_int2(s, q);
+      reinterpret_cast<int2*>(st.miss)[u] = make_int2(s, pos);
+      if (q >= 0) {
+        st.pos2slot[q] = -1;
+        ++nev;
+      }
+      st.pos2slot[pos] = s;
+      s2p[s] = pos;
+      out[missi[u]] = s;
+      missi[u] = s;  // from here on: the slot the j-th miss is fetched into
+      atomicOr(&bitmap[s >> 5], 1u << (s & 31));
     } else {
-      st.order[u - M] = o[r];  // kept: old relative order, at the front
+      st.order[u - M] = s;  // kept: old relative order, at the front
     }
   }
-  __syncthreads();  // victims and the referenced-or-refilled bitmap complete
+  nev = wave_inclusive_scan(nev);  // lane 63 holds the wave's total
+  if (lane == 63 && nev) atomicAdd(&misc[4], nev);
+  lds_barrier();  // 3: bitmap = referenced or refilled slots; s2p updated
 
-  // ---- Phase D: the j-th miss takes the j-th victim; update the maps -------
-  int nev = 0;
-#pragma unroll
-  for (int r = 0; r < IPT; ++r) {
-    if (cls[r] != kMiss) continue;
-    const int i = r * BD + tid;
-    const int j = jm[r];
-    const int s = victim[j];
-    const int q = s2p[s];
-    reinterpret_cast<int2*>(st.evict)[j] = make_int2(s, q);
-    if (q >= 0) {
-      st.pos2slot[q] = -1;
-      ++nev;
-    }
-    st.pos2slot[p[r]] = s;
-    st.slot2pos[s] = p[r];
-    st.last_use[s] = t;
-    out[i] = s;
-    reinterpret_cast<int2*>(st.miss)[j] = make_int2(s, p[r]);
-  }
-  nev = wave_sum(nev);
-  if (lane == 0 && nev) atomicAdd(&misc[4], nev);
-
-  // ---- Phase E: referenced-or-refilled slots go to the back, by slot -------
+  // ---- referenced-or-refilled slots go to the back of the LRU order, by ----
+  // slot number; their last_use and slot2pos are written densely.  Chunk
+  // e = r*W + w covers slots [64e, 64e + 64) = bitmap words 2e and 2e + 1.
+  const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
     const int x = r * BD + tid;
     flag[r] = (x < C) && test_bit(bitmap, x);
+    pre[r] = __popcll(__ballot(flag[r]) & lt);
   }
-  ballot_counts<IPT>(flag, cntC, W, wave, lane, pre);
-  __syncthreads();
-  wave_offsets<IPT>(cntC, W, wave, lane, off);
+  scan_offsets<IPT>(
+      [&](int e) {
+        const int w0 = 2 * e;
+        return (w0 < nbm ? __popc(bitmap[w0]) : 0) + (w0 + 1 < nbm ? __popc(bitmap[w0 + 1]) : 0);
+      },
+      W, wave, lane, off);
   const int base = C - (n_hit + M);
 #pragma unroll
-  for (int r = 0; r < IPT; ++r)
-    if (flag[r]) st.order[base + off[r] + pre[r]] = r * BD + tid;
+  for (int r = 0; r < IPT; ++r) {
+    if (!flag[r]) continue;
+    const int x = r * BD + tid;
+    st.order[base + off[r] + pre[r]] = x;
+    st.last_use[x] = t;
+    st.slot2pos[x] = s2p[x];
+  }
 
   if (tid == 0) {
+    const int n_evict = misc[4];
     st.hdr[kHdrT] = t;
     st.hdr[kHdrStatus] = 0;
     st.hdr[kHdrPad] = misc[1];
     st.hdr[kHdrRes] = misc[2];
     st.hdr[kHdrHit] = n_hit;
     st.hdr[kHdrMiss] = M;
-    st.hdr[kHdrEvict] = misc[4];
+    st.hdr[kHdrEvict] = n_evict;
     st.hdr[kHdrBytes] = (v.flags & HISPARSE_NO_IO) ? 0 : (int32_t)(M * v.row_bytes);
-    *reinterpret_cast<int64_t*>(st.hdr + kHdrTotalMiss) += M;
-    *reinterpret_cast<int64_t*>(st.hdr + kHdrTotalEvict) += misc[4];
-    *reinterpret_cast<int64_t*>(st.hdr + kHdrTotalHit) += n_hit;
+    *reinterpret_cast<int64_t*>(st.hdr + kHdrTotalMiss) = tot_miss + M;
+    *reinterpret_cast<int64_t*>(st.hdr + kHdrTotalEvict) = tot_evict + n_evict;
+    *reinterpret_cast<int64_t*>(st.hdr + kHdrTotalHit) = tot_hit + n_hit;
+  }
+
+  // ---- fused miss fetch: the workgroup copies its own missing rows ---------
+  // (enough in flight to saturate the host link once a layer call has >= 8
+  // streams; with fewer, the separate fan-out fetch kernel is used instead)
+  if (v.fuse_fetch && !(v.flags & HISPARSE_NO_IO)) {
+    constexpr int U = 4;
+    const uint32_t cpr = (uint32_t)(v.row_bytes >> 4);
+    const uint32_t total = (uint32_t)M * cpr;
+    const uint8_t* host = v.host[layer * v.B + b];
+    uint8_t* dst = v.cache + (int64_t)(layer * v.B + b) * (C + R) * v.row_bytes;
+    for (uint32_t g0 = tid; g0 < total; g0 += BD * U) {
+      u32x4 val[U];
+      int sl[U];
+      uint32_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t g = g0 + u * BD;
+        if (g < total) {
+          const uint32_t j = fast_div(g, cpr, v.cpr_magic, &c[u]);
+          sl[u] = missi[j];
+          val[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(host + (int64_t)missp[j] * v.row_bytes) + c[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t g = g0 + u * BD;
+        if (g < total) reinterpret_cast<u32x4*>(dst + (int64_t)sl[u] * v.row_bytes)[c[u]] = val[u];
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Miss fetch: copy every listed row from the host history into its slot.
-// grid = (grid_x, B); each workgroup strides over its stream's 16-byte chunks.
+// Miss fetch: copy every listed row of every stream of `layer` from the host
+// history into its slot.  The 16-byte chunks of all streams' misses form one
+// flat index space, split evenly over the grid, so no stream's tail is left
+// to a few CUs (one CU pulls only ~1/5 of the link).  grid = (G); LDS holds
+// the per-stream chunk prefix.
 // ---------------------------------------------------------------------------
 template <int U>
 __global__ void __launch_bounds__(kFetchThreads) fetch_kernel(StreamView v, int layer) {
-  const int b = blockIdx.y;
-  const StreamPtrs st = stream_ptrs(v, layer, b);
-  const int M = st.hdr[kHdrMiss];
+  extern __shared__ int lds[];
+  uint32_t* pre = reinterpret_cast<uint32_t*>(lds);  // [B + 1] chunk prefix
+  const int B = v.B;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const uint32_t cpr = (uint32_t)(v.row_bytes >> 4);
-  const uint32_t total = (uint32_t)M * cpr;
-  const uint32_t first = blockIdx.x * (kFetchThreads * U);
-  if (first >= total) return;
-  const int2* ml = reinterpret_cast<const int2*>(st.miss);
-  const uint8_t* host = v.host[layer * v.B + b];
-  uint8_t* dst = v.cache + (int64_t)(layer * v.B + b) * (v.C + v.R) * v.row_bytes;
-  const uint32_t stride = gridDim.x * (kFetchThreads * U);
-  for (uint32_t g0 = first + threadIdx.x; g0 < total; g0 += stride) {
+  if (tid < 64) {  // one wave scans the per-stream miss counts
+    uint32_t carry = 0;
+    for (int c = 0; c < B; c += 64) {
+      const int bb = c + lane;
+      const int m = bb < B ? stream_ptrs(v, layer, bb).hdr[kHdrMiss] : 0;
+      const int incl = wave_inclusive_scan(m);
+      if (bb < B) pre[bb + 1] = carry + (uint32_t)incl * cpr;
+      carry += (uint32_t)__builtin_amdgcn_readlane(incl, 63) * cpr;
+    }
+    if (tid == 0) pre[0] = 0;
+  }
+  lds_barrier();
+  const uint32_t total = pre[B];
+  const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
+  const uint32_t start = blockIdx.x * per;
+  const uint32_t end = start + per < total ? start + per : total;
+  for (uint32_t g0 = start + tid; g0 < end; g0 += kFetchThreads * U) {
     u32x4 val[U];
-    int2 e[U];
-    uint32_t c[U];
+    uint8_t* dst[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t g = g0 + u * kFetchThreads;
-      if (g < total) {
-        const uint32_t j = g / cpr;
-        c[u] = g - j * cpr;
-        e[u] = ml[j];
+      dst[u] = nullptr;
+      if (g < end) {
+        int lo = 0, hi = B;  // largest b with pre[b] <= g
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pre[mid] <= g) lo = mid; else hi = mid;
+        }
+        const StreamPtrs st = stream_ptrs(v, layer, lo);
+        uint32_t c;
+        const uint32_t j = fast_div(g - pre[lo], cpr, v.cpr_magic, &c);
+        const int2 e = reinterpret_cast<const int2*>(st.miss)[j];
+        const uint8_t* host = v.host[layer * B + lo];
+        dst[u] = v.cache + ((int64_t)(layer * B + lo) * (v.C + v.R) + e.x) * v.row_bytes + 16 * c;
         val[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(host + (int64_t)e[u].y * v.row_bytes) + c[u]);
+            reinterpret_cast<const u32x4*>(host + (int64_t)e.y * v.row_bytes) + c);
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t g = g0 + u * kFetchThreads;
-      if (g < total)
-        reinterpret_cast<u32x4*>(dst + (int64_t)e[u].x * v.row_bytes)[c[u]] = val[u];
-    }
+    for (int u = 0; u < U; ++u)
+      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
   }
 }
 
@@ -420,7 +538,8 @@ __global__ void load_window_kernel(StreamView v, int layer0, const int32_t* __re
   uint8_t* dst = v.cache + (int64_t)(layer * v.B + b) * (v.C + v.R) * v.row_bytes;
   for (uint32_t g = blockIdx.x * blockDim.x + threadIdx.x; g < total;
        g += gridDim.x * blockDim.x) {
-    const uint32_t r = g / cpr, c = g - r * cpr;
+    uint32_t c;
+    const uint32_t r = fast_div(g, cpr, v.cpr_magic, &c);
     const int32_t pos = lo + (int32_t)r;
     const u32x4 val = __builtin_nontemporal_load(
         reinterpret_cast<const u32x4*>(host + (int64_t)pos * v.row_bytes) + c);
@@ -510,7 +629,7 @@ ResolveShape resolve_shape(int k, int C, bool debug_validate) {
   }
   if (s.items == 0) return s;
   const int W = s.threads / 64;
-  size_t words = (size_t)((C + 31) / 32) + C + k + 3 * (size_t)s.items * W + 8;
+  size_t words = (size_t)((C + 31) / 32) + C + 2 * (size_t)k + 2 * (size_t)s.items * W + 8;
   if (debug_validate) words += (size_t)(2 << (31 - __builtin_clz((unsigned)k)));
   s.lds_bytes = 4 * words;
   return s;
@@ -547,8 +666,9 @@ hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const i
   return hipGetLastError();
 }
 
-hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid_x) {
-  hipLaunchKernelGGL(fetch_kernel<4>, dim3(grid_x, v.B), dim3(kFetchThreads), 0, s, v, layer);
+hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid) {
+  hipLaunchKernelGGL(fetch_kernel<4>, dim3(grid), dim3(kFetchThreads), sizeof(int) * (v.B + 1), s,
+                     v, layer);
   return hipGetLastError();
 }
 

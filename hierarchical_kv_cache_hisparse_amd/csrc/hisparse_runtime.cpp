@@ -53,6 +53,9 @@ int validate_config(const hisparse_config* c) {
   if (!c) return fail(HISPARSE_ERR_INVALID_ARG, "config is NULL");
   if (c->num_requests < 1 || c->num_layers < 1)
     return fail(HISPARSE_ERR_INVALID_ARG, "num_requests and num_layers must be >= 1");
+  if (c->num_requests > kMaxRequests)
+    return fail(HISPARSE_ERR_UNSUPPORTED, "num_requests %d exceeds %d", c->num_requests,
+                kMaxRequests);
   if (c->max_positions < 1 || c->max_positions >= (int64_t(1) << 31))
     return fail(HISPARSE_ERR_INVALID_ARG, "max_positions must be in [1, 2^31)");
   if (c->row_bytes <= 0 || c->row_bytes % 16 != 0)
@@ -108,7 +111,7 @@ struct hisparse {
   int32_t* pf_sel = nullptr;     // [L][B][k] prefetched selections
   std::vector<uint8_t> pending;  // per layer: a prefetch waits to be joined
   std::vector<hipEvent_t> ev_fork, ev_done;
-  int fetch_grid_x = 1;
+  int fetch_grid_x = 64;  // fetch kernel workgroups
   // timing of eager calls
   bool timing = false;
   std::vector<TimedCall> pool;
@@ -153,12 +156,12 @@ int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_
       if (rc) return rc;
     }
     tc = &h->pool[h->pool_used++];
-    tc->fetched = io;
+    tc->fetched = io && !h->view.fuse_fetch;
     HIP_TRY(hipEventRecord(tc->e0, s));
   }
   HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy));
   if (tc) HIP_TRY(hipEventRecord(tc->e1, s));
-  if (io) HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
+  if (io && !h->view.fuse_fetch) HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
   if (tc) HIP_TRY(hipEventRecord(tc->e2, s));
   return HISPARSE_OK;
 }
@@ -265,6 +268,18 @@ int hisparse_create(const hisparse_config* cfg, void* const* host_rows, void* de
   h->lay = meta_layout(*cfg);
   hipError_t e = hipGetDevice(&h->device);
   if (e != hipSuccess) { release(h); return hip_fail(e, "hipGetDevice"); }
+  {
+    int lds_max = 0;
+    e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, h->device);
+    if (e != hipSuccess) { release(h); return hip_fail(e, "hipDeviceGetAttribute"); }
+    const ResolveShape sh =
+        resolve_shape(cfg->top_k, cfg->cache_slots, (cfg->flags & HISPARSE_DEBUG_VALIDATE) != 0);
+    if (sh.lds_bytes > (size_t)lds_max) {
+      release(h);
+      return fail(HISPARSE_ERR_UNSUPPORTED, "C=%d, k=%d need %zu bytes of LDS; the device has %d",
+                  cfg->cache_slots, cfg->top_k, sh.lds_bytes, lds_max);
+    }
+  }
   h->pending.assign(L, 0);
   h->ev_fork.assign(L, nullptr);
   h->ev_done.assign(L, nullptr);
@@ -307,10 +322,21 @@ int hisparse_create(const hisparse_config* cfg, void* const* host_rows, void* de
   v.k = cfg->top_k;
   v.l_cap = (int32_t)cfg->max_positions;
   v.flags = cfg->flags;
+  v.r_magic = div_magic((uint32_t)cfg->resident_window);
+  v.cpr_magic = div_magic((uint32_t)(cfg->row_bytes / 16));
 
-  // Fetch fan-out: about `wgs` workgroups in total, split over the requests.
-  const int wgs = env_int("HISPARSE_FETCH_WORKGROUPS", 1024);
-  h->fetch_grid_x = wgs / B > 1 ? wgs / B : 1;
+  // Miss fetch.  One CU pulls ~12 GB/s from pinned host memory and ~8 CUs
+  // saturate a PCIe Gen5 x16 link, so with >= 8 streams per layer call the
+  // resolve workgroups copy their own misses (no second launch, copies start
+  // as soon as the victims are known); with fewer, a separate kernel fans the
+  // copies out over ~64 workgroups.  HISPARSE_FETCH_MODE=fused|split forces
+  // a mode; HISPARSE_FETCH_WORKGROUPS sets the fan-out.
+  const char* mode = getenv("HISPARSE_FETCH_MODE");
+  if (mode && !strcmp(mode, "fused")) v.fuse_fetch = 1;
+  else if (mode && !strcmp(mode, "split")) v.fuse_fetch = 0;
+  else v.fuse_fetch = B >= 8 ? 1 : 0;
+  const int wgs = env_int("HISPARSE_FETCH_WORKGROUPS", 64);
+  h->fetch_grid_x = wgs > 1 ? wgs : 1;
 
   e = launch_init(v, nullptr, -1, -1, true);
   if (e == hipSuccess) e = hipStreamSynchronize(nullptr);

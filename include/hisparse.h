@@ -89,7 +89,7 @@ extern "C" {
 
 /* Shape of one cache instance.  All streams share it. */
 typedef struct hisparse_config {
-  int32_t num_requests;    /* B: request slots (>= 1)                        */
+  int32_t num_requests;    /* B: request slots, 1..32768                     */
   int32_t num_layers;      /* layers, each with its own cache (>= 1)         */
   int64_t max_positions;   /* host rows per stream (tokens or pages), < 2^31 */
   int32_t row_bytes;       /* bytes per row, a positive multiple of 16       */

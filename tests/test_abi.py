@@ -80,8 +80,12 @@ def test_invalid_configs_are_rejected_on_the_host(field, value, code):
     assert hb.hisparse_last_error()
 
 
-def test_lds_limit_is_enforced():
+def test_largest_shape_fits_the_lds():
+    """C = 16384 and k = 4096 with the debug hash is the largest shape; its
+    resolve workgroup still fits gfx950's 160 KiB of LDS."""
     cfg = hb.make_config(1, 1, 1 << 20, 1152, 16384, 0, 4096, hb.HISPARSE_DEBUG_VALIDATE)
+    hb.hisparse_workspace_bytes(cfg)
+    cfg.cache_slots = 16385
     with pytest.raises(hb.HisparseError) as e:
         hb.hisparse_workspace_bytes(cfg)
     assert e.value.code == hb.HISPARSE_ERR_UNSUPPORTED

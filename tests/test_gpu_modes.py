@@ -1,0 +1,381 @@
+"""GPU mode tests of the resolve path, all through the C ABI:
+
+  graph replay equals eager launches (the step is graph-capturable);
+  prefetch on a second stream equals no prefetch (exact layer-wise prefetch);
+  copies suppressed (no-IO) leave the metadata unchanged and read no rows;
+  hits read no host bytes (host rows of cached positions are poisoned);
+  invalid rows leave their stream untouched and are reported;
+  snapshot / restore of the caller-owned state replays identically;
+  resetting one request's stream leaves the others alone.
+"""
+import numpy as np
+import pytest
+
+from workload import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _hb():
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    return hb
+
+
+def _pair(cfg, flags_a=0, flags_b=0):
+    """Two instances over the same pinned host histories."""
+    from tests.gpu_harness import GpuInstance
+    from tests.harness import fill_host, make_trace
+    a = GpuInstance(cfg, flags=flags_a)
+    b = GpuInstance(cfg, flags=flags_b, hosts=a.hosts)
+    trace = make_trace(cfg)
+    fill_host(cfg, a.host, trace, [(bb, l) for bb in range(cfg.B) for l in range(cfg.layers)])
+    return a, b, trace
+
+
+def _assert_same_state(a, b, cfg, contents=True):
+    for l in range(cfg.layers):
+        for bb in range(cfg.B):
+            sa, sb = a.state(bb, l), b.state(bb, l)
+            for key in ("hdr", "slot2pos", "last_use", "order", "pos2slot"):
+                np.testing.assert_array_equal(sa[key], sb[key], err_msg=f"{key} (b={bb}, l={l})")
+            m = int(sa["hdr"][5])
+            np.testing.assert_array_equal(sa["evict"][:m], sb["evict"][:m])
+            if contents:
+                filled = np.nonzero(sa["slot2pos"] >= 0)[0]
+                np.testing.assert_array_equal(a.slots(bb, l)[filled], b.slots(bb, l)[filled])
+
+
+def _load_windows(inst, ctx_dev):
+    _hb().hisparse_load_window(inst.h, inst.stream, -1, ctx_dev.data_ptr())
+
+
+def test_graph_replay_equals_eager():
+    """One captured graph (reading the selections from a fixed buffer) is
+    replayed every step, with eager copies and synchronizations in between;
+    every replay must equal an eager instance bit for bit."""
+    torch, hb = _torch(), _hb()
+    cfg = CONFIGS[3].scaled(B=3, layers=2, L0=9000, C=2048, k=1024, steps=8)
+    a, b, trace = _pair(cfg)
+    try:
+        dev = "cuda:0"
+        ctx = torch.full((cfg.B,), cfg.ctx_at(0), dtype=torch.int32, device=dev)
+        _load_windows(a, ctx)
+        _load_windows(b, ctx)
+        sel_buf = torch.empty((cfg.layers, cfg.B, cfg.k), dtype=torch.int32, device=dev)
+        ctx_buf = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
+        out_g = torch.empty_like(sel_buf)
+        out_e = torch.empty_like(sel_buf)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                s = torch.cuda.current_stream().cuda_stream
+                for l in range(cfg.layers):
+                    hb.hisparse_resolve(a.h, s, sel_buf[l].data_ptr(), ctx_buf.data_ptr(), l,
+                                        out_g[l].data_ptr())
+        torch.cuda.synchronize()
+        trace_dev = torch.from_numpy(trace).to(dev)
+        from tests.harness import appended_row
+        for step in range(cfg.steps):
+            if step > 0:   # growth: append through the library on both instances
+                p = cfg.ctx_at(step) - 1
+                pos = torch.full((cfg.B,), p, dtype=torch.int32, device=dev)
+                for l in range(cfg.layers):
+                    rows = torch.from_numpy(np.stack([appended_row(cfg, bb, l, p)
+                                                      for bb in range(cfg.B)])).to(dev)
+                    hb.hisparse_append(a.h, a.stream, l, rows.data_ptr(), pos.data_ptr())
+                    hb.hisparse_append(b.h, b.stream, l, rows.data_ptr(), pos.data_ptr())
+            sel_buf.copy_(trace_dev[step])
+            ctx_buf.fill_(cfg.ctx_at(step))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for l in range(cfg.layers):
+                hb.hisparse_resolve(b.h, b.stream, trace_dev[step, l].data_ptr(),
+                                    ctx_buf.data_ptr(), l, out_e[l].data_ptr())
+            torch.cuda.synchronize()
+            assert torch.equal(out_g, out_e), f"step {step}"
+            _assert_same_state(a, b, cfg)
+        assert a.status() == 0 and b.status() == 0
+    finally:
+        b.close()
+        a.close()
+
+
+@pytest.mark.parametrize("captured", [False, True])
+def test_prefetch_equals_no_prefetch(captured):
+    """Shared selections across layers: layer l+1 resolved early on a second
+    stream (forked after layer l) must give the same slot maps and state as
+    resolving every layer in order on one stream."""
+    torch, hb = _torch(), _hb()
+    cfg = CONFIGS[4].scaled(B=2, layers=4, L0=30000, steps=6)
+    a, b, trace = _pair(cfg)
+    try:
+        dev = "cuda:0"
+        ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device=dev)
+        _load_windows(a, ctx)
+        _load_windows(b, ctx)
+        trace_dev = torch.from_numpy(trace).to(dev)
+        sel_buf = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=dev)
+        out_p = torch.empty((cfg.layers, cfg.B, cfg.k), dtype=torch.int32, device=dev)
+        out_s = torch.empty_like(out_p)
+        main = torch.cuda.Stream()
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+
+        def prefetched_step():
+            ms, ss = main.cuda_stream, side.cuda_stream
+            hb.hisparse_resolve(a.h, ms, sel_buf.data_ptr(), ctx.data_ptr(), 0, out_p[0].data_ptr())
+            for l in range(cfg.layers - 1):
+                hb.hisparse_prefetch(a.h, ms, ss, sel_buf.data_ptr(), ctx.data_ptr(), l + 1)
+                # (layer l's attention would run on `main` here)
+                hb.hisparse_resolve(a.h, ms, sel_buf.data_ptr(), ctx.data_ptr(), l + 1,
+                                    out_p[l + 1].data_ptr())
+
+        graph = None
+        if captured:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(main):
+                with torch.cuda.graph(graph, stream=main):
+                    prefetched_step()
+            torch.cuda.synchronize()
+        for step in range(cfg.steps):
+            sel_buf.copy_(trace_dev[step, 0])
+            torch.cuda.synchronize()
+            if captured:
+                graph.replay()
+            else:
+                with torch.cuda.stream(main):
+                    prefetched_step()
+            torch.cuda.synchronize()
+            for l in range(cfg.layers):
+                hb.hisparse_resolve(b.h, b.stream, sel_buf.data_ptr(), ctx.data_ptr(), l,
+                                    out_s[l].data_ptr())
+            torch.cuda.synchronize()
+            assert torch.equal(out_p, out_s), f"step {step}"
+            _assert_same_state(a, b, cfg)
+            # shared selections: every layer ends in the same state
+            for l in range(1, cfg.layers):
+                assert torch.equal(out_s[0], out_s[l])
+        assert a.status() == 0 and b.status() == 0
+    finally:
+        b.close()
+        a.close()
+
+
+def test_prefetch_misuse_is_reported():
+    torch, hb = _torch(), _hb()
+    cfg = CONFIGS[4].scaled(B=2, layers=2, L0=5000, steps=2)
+    from tests.gpu_harness import GpuInstance
+    g = GpuInstance(cfg)
+    try:
+        dev = "cuda:0"
+        ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device=dev)
+        sel = torch.from_numpy(np.stack([np.random.default_rng(b).choice(cfg.L0 - 100, cfg.k,
+                                        replace=False) for b in range(cfg.B)]).astype(np.int32)).to(dev)
+        other = sel.flip(1).contiguous()
+        out = torch.empty_like(sel)
+        s = g.stream
+        side = torch.cuda.Stream()
+        hb.hisparse_prefetch(g.h, s, side.cuda_stream, sel.data_ptr(), ctx.data_ptr(), 1)
+        with pytest.raises(hb.HisparseError) as e:
+            hb.hisparse_prefetch(g.h, s, side.cuda_stream, sel.data_ptr(), ctx.data_ptr(), 1)
+        assert e.value.code == hb.HISPARSE_ERR_STATE
+        hb.hisparse_resolve(g.h, s, other.data_ptr(), ctx.data_ptr(), 1, out.data_ptr())
+        torch.cuda.synchronize()
+        assert g.status(clear=True) & hb.HISPARSE_STATUS_PREFETCH_MISMATCH
+        assert g.status() == 0
+    finally:
+        g.close()
+
+
+def test_no_io_equals_io_metadata_and_reads_nothing():
+    torch, hb = _torch(), _hb()
+    cfg = CONFIGS[2].scaled(B=4, L0=20000, steps=10)
+    a, b, trace = _pair(cfg, 0, hb.HISPARSE_NO_IO)
+    try:
+        dev = "cuda:0"
+        ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device=dev)
+        _load_windows(a, ctx)
+        b.cache.fill_(0xA5)           # no-IO instance: LRU slots must never change
+        _load_windows(b, ctx)
+        trace_dev = torch.from_numpy(trace).to(dev)
+        out_a = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=dev)
+        out_b = torch.empty_like(out_a)
+        for step in range(cfg.steps):
+            hb.hisparse_resolve(a.h, a.stream, trace_dev[step, 0].data_ptr(), ctx.data_ptr(), 0,
+                                out_a.data_ptr())
+            hb.hisparse_resolve(b.h, b.stream, trace_dev[step, 0].data_ptr(), ctx.data_ptr(), 0,
+                                out_b.data_ptr())
+            torch.cuda.synchronize()
+            assert torch.equal(out_a, out_b)
+            for bb in range(cfg.B):
+                sa, sb = a.state(bb, 0), b.state(bb, 0)
+                for key in ("slot2pos", "last_use", "order", "pos2slot"):
+                    np.testing.assert_array_equal(sa[key], sb[key])
+                np.testing.assert_array_equal(sa["hdr"][:7], sb["hdr"][:7])
+                assert sb["hdr"][7] == 0 and sa["hdr"][7] == sa["hdr"][5] * cfg.row_bytes
+                assert (b.slots(bb, 0)[: cfg.C] == 0xA5).all()
+    finally:
+        b.close()
+        a.close()
+
+
+@pytest.mark.parametrize("noncoherent", [False, True])
+def test_hits_read_no_host_bytes(noncoherent):
+    """After every step the host rows of every cached position are poisoned;
+    hit slots must keep the bytes fetched earlier, and every slot must still
+    match the oracle reading the same (poisoned) host memory."""
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import LockstepRun
+    cfg = CONFIGS[2].scaled(B=2, L0=12000, C=1024, k=512, steps=10)
+    flags = hb.HISPARSE_HOST_NONCOHERENT if noncoherent else hb.HISPARSE_HOST_COHERENT
+    run = LockstepRun(cfg, host_flags=flags)
+    try:
+        before = {}
+        for s in range(cfg.steps):
+            run.gpu_step(s)
+            torch.cuda.synchronize()
+            res = run.oracle_step(s)
+            run.compare_step(s, res, host_rows=False)   # host rows are poisoned on purpose
+            for (b, l), r in res.items():
+                st = run.oracle.st[(b, l)]
+                dev = run.gpu.slots(b, l)
+                fetched = set(r.log_slot.tolist())
+                hit_slots = [x for x in r.out.tolist() if 0 <= x < cfg.C and x not in fetched]
+                for x in hit_slots:                       # bytes from before the poisoning
+                    assert (dev[x] == before[(b, l)][x]).all(), f"hit slot {x} re-read host memory"
+                held = st.slot2pos[st.slot2pos >= 0]
+                run.gpu.host(b, l)[held] ^= 0x5A          # poison every cached position
+                before[(b, l)] = dev.copy()
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+
+
+def test_invalid_rows_are_rejected_per_request():
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import GpuInstance
+    cfg = CONFIGS[2].scaled(B=3, L0=6000, C=512, k=256, steps=1)
+    for flags in (0, hb.HISPARSE_DEBUG_VALIDATE):
+        g = GpuInstance(cfg, flags=flags)
+        try:
+            dev = "cuda:0"
+            rng = np.random.default_rng(11)
+            sel = np.stack([rng.choice(cfg.L0, cfg.k, replace=False) for _ in range(cfg.B)]).astype(np.int32)
+            ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device=dev)
+            out = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=dev)
+            # a clean first step everywhere
+            hb.hisparse_resolve(g.h, g.stream, torch.from_numpy(sel).to(dev).data_ptr(),
+                                ctx.data_ptr(), 0, out.data_ptr())
+            torch.cuda.synchronize()
+            snap = [g.state(b, 0) for b in range(cfg.B)]
+            bad = sel.copy()
+            bad[1, 17] = cfg.L0                  # out of range in request 1
+            expect = hb.HISPARSE_STATUS_SEL_RANGE
+            if flags & hb.HISPARSE_DEBUG_VALIDATE:
+                bad[2, 5] = bad[2, 9]            # repeated position in request 2
+                expect |= hb.HISPARSE_STATUS_SEL_DUP
+            hb.hisparse_resolve(g.h, g.stream, torch.from_numpy(bad).to(dev).data_ptr(),
+                                ctx.data_ptr(), 0, out.data_ptr())
+            torch.cuda.synchronize()
+            o = out.cpu().numpy()
+            assert (o[1] == -1).all()
+            st1 = g.state(1, 0)
+            for key in ("slot2pos", "last_use", "order", "pos2slot"):
+                np.testing.assert_array_equal(st1[key], snap[1][key])
+            assert st1["hdr"][0] == snap[1]["hdr"][0]          # clock not advanced
+            assert st1["hdr"][1] == hb.HISPARSE_STATUS_SEL_RANGE
+            assert g.state(0, 0)["hdr"][0] == snap[0]["hdr"][0] + 1   # request 0 ran
+            if flags & hb.HISPARSE_DEBUG_VALIDATE:
+                assert (o[2] == -1).all() and g.state(2, 0)["hdr"][1] == hb.HISPARSE_STATUS_SEL_DUP
+            assert g.status(clear=True) == expect
+            # a bad context length
+            ctx_bad = torch.tensor([cfg.L0, cfg.l_cap + 1, -3], dtype=torch.int32, device=dev)
+            hb.hisparse_resolve(g.h, g.stream, torch.from_numpy(sel).to(dev).data_ptr(),
+                                ctx_bad.data_ptr(), 0, out.data_ptr())
+            torch.cuda.synchronize()
+            assert g.status(clear=True) & hb.HISPARSE_STATUS_CTX_RANGE
+            o = out.cpu().numpy()
+            assert (o[1] == -1).all() and (o[2] == -1).all() and (o[0] >= 0).all()
+        finally:
+            g.close()
+
+
+def test_snapshot_restore_replays_identically():
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import LockstepRun
+    cfg = CONFIGS[2].scaled(B=2, L0=15000, steps=12)
+    run = LockstepRun(cfg)
+    try:
+        for s in range(5):
+            run.gpu_step(s)
+        torch.cuda.synchronize()
+        meta0, cache0 = run.gpu.meta.clone(), run.gpu.cache.clone()
+        outs = []
+        for s in range(5, cfg.steps):
+            run.gpu_step(s)
+            torch.cuda.synchronize()
+            outs.append(run.out_dev.clone())
+        meta1, cache1 = run.gpu.meta.clone(), run.gpu.cache.clone()
+        run.gpu.meta.copy_(meta0)
+        run.gpu.cache.copy_(cache0)
+        torch.cuda.synchronize()
+        for i, s in enumerate(range(5, cfg.steps)):
+            run.gpu_step(s)
+            torch.cuda.synchronize()
+            assert torch.equal(run.out_dev, outs[i]), f"step {s}"
+        assert torch.equal(run.gpu.meta, meta1) and torch.equal(run.gpu.cache, cache1)
+    finally:
+        run.close()
+
+
+def test_reset_one_request_leaves_the_others():
+    torch, hb = _torch(), _hb()
+    from oracle.oracle import OracleStream
+    from tests.gpu_harness import LockstepRun
+    cfg = CONFIGS[3].scaled(B=3, layers=2, L0=8000, C=1024, k=512, steps=8, growth=0)
+    run = LockstepRun(cfg)
+    try:
+        for s in range(4):
+            run.gpu_step(s)
+            torch.cuda.synchronize()
+            run.compare_step(s, run.oracle_step(s))
+        hb.hisparse_reset(run.gpu.h, run.gpu.stream, 1, 2)     # layer 1, request 2
+        torch.cuda.synchronize()
+        st = run.gpu.state(2, 1)
+        assert (st["slot2pos"] == -1).all() and (st["pos2slot"] == -1).all()
+        assert (st["last_use"] == 0).all() and (st["order"] == np.arange(cfg.C)).all()
+        assert st["hdr"][0] == 0
+        fresh = OracleStream(cfg.C, cfg.R, cfg.l_cap, cfg.row_bytes, host=run.gpu.host(2, 1))
+        fresh.slots[:] = run.oracle.st[(2, 1)].slots   # the ring slots are not reset
+        run.oracle.st[(2, 1)] = fresh
+        for s in range(4, cfg.steps):
+            run.gpu_step(s)
+            torch.cuda.synchronize()
+            run.compare_step(s, run.oracle_step(s))
+    finally:
+        run.close()
+
+
+def test_timing_counts_every_launch():
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import LockstepRun
+    cfg = CONFIGS[3].scaled(B=2, layers=3, L0=5000, C=1024, k=512, steps=4, growth=0)
+    run = LockstepRun(cfg, oracle_streams=[])
+    try:
+        hb.hisparse_set_timing(run.gpu.h, True)
+        for s in range(cfg.steps):
+            run.gpu_step(s)
+        t = hb.hisparse_get_timing(run.gpu.h)
+        assert t["resolve_launches"] == cfg.steps * cfg.layers
+        assert t["fetch_launches"] == cfg.steps * cfg.layers
+        assert t["resolve_ms"] > 0 and t["fetch_ms"] > 0
+    finally:
+        run.close()

@@ -44,6 +44,21 @@ CASES = {
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_parity_reduced(name):
     base, kw = CASES[name]
+    _parity_case(name, base, kw)
+
+
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("name", ["one_request_ragged", "independent_layers_growth", "pages",
+                                  "largest_supported_shape"])
+def test_parity_fetch_modes(name, mode, monkeypatch):
+    """Both miss-fetch paths (copies by the resolve workgroups themselves, or
+    by a separate fan-out kernel) on the same cases."""
+    monkeypatch.setenv("HISPARSE_FETCH_MODE", mode)
+    base, kw = CASES[name]
+    _parity_case(name, base, kw)
+
+
+def _parity_case(name, base, kw):
     cfg = CONFIGS[base].scaled(**kw)
     print(f"[parity] {name}: B={cfg.B} L={cfg.layers} L0={cfg.L0} C={cfg.C} R={cfg.R} "
           f"k={cfg.k} steps={cfg.steps}", flush=True)
