@@ -48,6 +48,13 @@ def parse_args():
                     help="only the eager timed region (for profiler runs)")
     ap.add_argument("--host-noncoherent", action="store_true",
                     help="allocate host histories non-coherent (GPU-cacheable)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed region, copy 256 MiB device->device with the "
+                         "library's 16-byte copy kernel (known bytes for PMC scaling)")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="summarize rocprofv3 CSV output in DIR into profiles/ and exit")
+    ap.add_argument("--label", help="summary name (with --summarize-rocprof)")
+    ap.add_argument("--command", help="the profiled command line (with --summarize-rocprof)")
     return ap.parse_args()
 
 
@@ -152,7 +159,7 @@ def link_probe(torch, hb):
         host_view(ptr, nbytes)[:] = 1
         stream = torch.cuda.current_stream().cuda_stream
         per_wg = {}
-        for wgs in (256, 1024, 4096):
+        for wgs in (1, 4, 8, 16, 64, 256, 1024):
             best = 0.0
             for _ in range(5):
                 torch.cuda.synchronize()
@@ -166,6 +173,107 @@ def link_probe(torch, hb):
         hb.hisparse_host_free(ptr)
     res["measured_peak_GBps"] = max(res["memcpy_h2d_GBps"], *res["zero_copy_read_GBps"].values())
     return res
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "hierarchical_kv_cache_hisparse_amd", "csrc",
+                             "hisparse_kernels.hip")
+CALIBRATION_BYTES = 256 << 20
+
+
+def kernel_source_sha():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def short_kernel_name(name):
+    for key in ("resolve_kernel", "fetch_kernel", "probe_host_read_kernel", "init_kernel",
+                "load_window_kernel", "append_kernel", "prefetch_join_kernel"):
+        if key in name:
+            return key
+    return name.split("(")[0][-48:]
+
+
+def summarize_rocprof(directory, label, command):
+    """Turn rocprofv3 CSV output (kernel trace + stats, or one PMC counter)
+    into a short Markdown summary under profiles/."""
+    import csv
+    import glob
+    lines = [f"# {label}", "", f"Command: `{command}`", "",
+             f"Kernel source sha256[:16]: {kernel_source_sha()}", ""]
+    stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    pmc = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if stats:
+        lines += ["## rocprofv3 --stats (kernel durations)", "",
+                  "| kernel | calls | total us | average us | min us | max us |",
+                  "|---|---|---|---|---|---|"]
+        with open(stats[0]) as f:
+            for row in csv.DictReader(f):
+                lines.append("| {} | {} | {:.1f} | {:.3f} | {:.3f} | {:.3f} |".format(
+                    short_kernel_name(row["Name"]), row["Calls"],
+                    float(row["TotalDurationNs"]) / 1e3, float(row["AverageNs"]) / 1e3,
+                    float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
+        lines.append("")
+    if trace:
+        import statistics
+        per = {}
+        with open(trace[0]) as f:
+            for row in csv.DictReader(f):
+                d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                per.setdefault(short_kernel_name(row["Kernel_Name"]), []).append(d)
+        lines += ["## kernel trace: per-launch durations (us)", "",
+                  "| kernel | launches | mean | median | first launch |", "|---|---|---|---|---|"]
+        for k, v in per.items():
+            lines.append(f"| {k} | {len(v)} | {statistics.mean(v):.3f} | "
+                         f"{statistics.median(v):.3f} | {v[0]:.3f} |")
+        lines.append("")
+    if pmc:
+        agg = {}
+        with open(pmc[0]) as f:
+            for row in csv.DictReader(f):
+                key = (short_kernel_name(row["Kernel_Name"]), row["Counter_Name"])
+                agg.setdefault(key, []).append(float(row["Counter_Value"]))
+        lines += ["## PMC counters (per dispatch)", "",
+                  "| kernel | counter | dispatches | mean per dispatch | total |",
+                  "|---|---|---|---|---|"]
+        for (k, c), v in sorted(agg.items()):
+            lines.append(f"| {k} | {c} | {len(v)} | {sum(v) / len(v):.1f} | {sum(v):.1f} |")
+        lines.append("")
+        for (k, c), v in sorted(agg.items()):
+            lines.append(f"pmc: kernel={k} counter={c} mean={sum(v) / len(v):.3f} "
+                         f"dispatches={len(v)}")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, label + ".md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def committed_traffic(kernel, cfg_name, mode):
+    """HBM+link bytes per launch of `kernel` from the committed PMC summaries
+    (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, each scaled by the counter's
+    reading for a device copy of known size), or None when absent or taken on
+    a different kernel source."""
+    import re
+    vals = {}
+    sha = kernel_source_sha()
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        path = os.path.join(PROFILES, f"pmc_{counter.lower()}_{cfg_name}_{mode}.md")
+        if not os.path.exists(path):
+            return None
+        text = open(path).read()
+        if f"Kernel source sha256[:16]: {sha}" not in text:
+            return None
+        got = {}
+        for m in re.finditer(r"pmc: kernel=(\S+) counter=(\S+) mean=([0-9.eE+-]+)", text):
+            got[m.group(1)] = float(m.group(3))
+        if kernel not in got or "probe_host_read_kernel" not in got:
+            return None
+        scale = (CALIBRATION_BYTES / 1024.0) / got["probe_host_read_kernel"]
+        vals[counter] = got[kernel] * scale * 1024.0
+    return vals
 
 
 def cpu_baseline(setup, steps):
@@ -193,6 +301,9 @@ def cpu_baseline(setup, steps):
 
 def main():
     args = parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.label or "profile", args.command or "")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the resolve path has no cross-GPU step, and this "
               f"build runs on a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -234,6 +345,16 @@ def main():
             f"{timing['resolve_launches']}, fetch {timing['fetch_ms']:.3f} ms / "
             f"{timing['fetch_launches']}")
 
+        if args.calibration_copy:
+            src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda:0")
+            dst = torch.empty_like(src)
+            src.fill_(3)
+            torch.cuda.synchronize()
+            hb.hisparse_probe_host_read(torch.cuda.current_stream().cuda_stream, src.data_ptr(),
+                                        dst.data_ptr(), CALIBRATION_BYTES, 1024)
+            torch.cuda.synchronize()
+            del src, dst
+
         fused = timing["fetch_launches"] == 0
         resolve_avg_s = timing["resolve_ms"] / max(1, timing["resolve_launches"]) / 1e3
         if fused:   # the resolve workgroups copy their own misses
@@ -251,7 +372,8 @@ def main():
         avg_hit = tot_hit / max(1, n_calls * cfg.B)
         meta_bytes = cfg.B * (12 * cfg.k + 16 * cfg.C + 4 * (avg_hit + avg_miss) + 24 * avg_miss + 64)
         resolve_gbps = meta_bytes / resolve_avg_s / 1e9 if resolve_avg_s > 0 else 0.0
-        dominant = "resolve_kernel (fused miss fetch)" if fused else "fetch_kernel"
+        dominant = "resolve_kernel" if fused else "fetch_kernel"
+        traffic = committed_traffic(dominant, f"cfg{args.config}", "fused" if fused else "split")
 
         result = {
             "metric": "resolved top-k entries/s; miss-fetch GB/s vs host-link peak; no-IO overhead",
@@ -271,10 +393,13 @@ def main():
                        "resident_window": cfg.R, "top_k": cfg.k, "steps": K,
                        "carry_over_pct": cfg.carry_pct, "replacement": cfg.replacement,
                        "timed_launch_mode": "eager, library HIP-event timing on"},
-            "roofline": {"bound": "host_link", "kernel": dominant,
+            "roofline": {"bound": "host_link", "kernel": dominant, "fused_fetch": fused,
                          "achieved": round(fetch_gbps, 3), "peak": LINK_PEAK_THEORETICAL_GBPS,
                          "unit": "GB/s", "frac": round(fetch_gbps / LINK_PEAK_THEORETICAL_GBPS, 4),
-                         "traffic": None,
+                         "traffic": (round(traffic["FETCH_SIZE"] + traffic["WRITE_SIZE"])
+                                     if traffic else None),
+                         "traffic_read_bytes": round(traffic["FETCH_SIZE"]) if traffic else None,
+                         "traffic_write_bytes": round(traffic["WRITE_SIZE"]) if traffic else None,
                          "per_launch_bytes": round(fetch_bytes_per_launch),
                          "avg_launch_us": round(fetch_avg_s * 1e6, 3)},
             "resolve_kernel": {"bound": "hbm", "fused_fetch": fused,
