@@ -39,7 +39,8 @@ BUDGET_LAYERS = 64                      # ... spread over a 64-layer model
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: the workload's own step count, 64 for workload 2)")
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -51,6 +52,11 @@ def parse_args():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the timed region, copy 256 MiB device->device with the "
                          "library's 16-byte copy kernel (known bytes for PMC scaling)")
+    ap.add_argument("--prefetch-study", action="store_true",
+                    help="shared-selection workloads: serial vs layer-wise prefetch vs no-IO, "
+                         "with a fixed-duration stand-in for each layer's compute")
+    ap.add_argument("--layer-compute-us", type=float, default=312.5,
+                    help="stand-in compute per layer for --prefetch-study (20 ms / 64 layers)")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="summarize rocprofv3 CSV output in DIR into profiles/ and exit")
     ap.add_argument("--label", help="summary name (with --summarize-rocprof)")
@@ -276,27 +282,113 @@ def committed_traffic(kernel, cfg_name, mode):
     return vals
 
 
-def cpu_baseline(setup, steps):
-    """The CPU oracle (plain C, one thread) on the same trace and host rows;
-    repeated from a cold state until at least 3 s of work are measured."""
+def prefetch_study(setup, K, compute_us):
+    """Exact layer-wise prefetch on a shared-selection workload.
+
+    Per layer a stand-in compute kernel (torch's fixed-cycle busy kernel,
+    calibrated to `compute_us`) runs on the main stream.  Three schedules,
+    each captured as one HIP graph of K steps and replayed from a cold cache:
+      serial:   resolve(l); compute(l)                       for every layer
+      prefetch: resolve(0); then per layer prefetch(l+1) on a side stream,
+                compute(l), resolve(l+1) joins it
+      no-IO:    the serial schedule with copies suppressed
+    hidden = 1 - (T_prefetch - T_noIO) / (T_serial - T_noIO).
+    """
+    torch, hb, cfg = setup.torch, setup.hb, setup.cfg
+    if not cfg.shared_selection:
+        raise SystemExit("--prefetch-study needs a workload whose layers share selections")
+    # calibrate the busy kernel
+    cycles = 1_000_000
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        ev0.record(); torch.cuda._sleep(cycles); ev1.record(); torch.cuda.synchronize()
+    us_per_cycle = ev0.elapsed_time(ev1) * 1e3 / cycles
+    cyc = max(1, int(round(compute_us / us_per_cycle)))
+
+    def serial(inst, s, ms, ss):
+        for l in range(cfg.layers):
+            hb.hisparse_resolve(inst.h, ms, setup.sel[s, l].data_ptr(), setup.ctx[s].data_ptr(), l,
+                                setup.out[l].data_ptr())
+            torch.cuda._sleep(cyc)
+
+    def prefetched(inst, s, ms, ss):
+        hb.hisparse_resolve(inst.h, ms, setup.sel[s, 0].data_ptr(), setup.ctx[s].data_ptr(), 0,
+                            setup.out[0].data_ptr())
+        for l in range(cfg.layers):
+            if l + 1 < cfg.layers:
+                hb.hisparse_prefetch(inst.h, ms, ss, setup.sel[s, l + 1].data_ptr(),
+                                     setup.ctx[s].data_ptr(), l + 1)
+            torch.cuda._sleep(cyc)
+            if l + 1 < cfg.layers:
+                hb.hisparse_resolve(inst.h, ms, setup.sel[s, l + 1].data_ptr(),
+                                    setup.ctx[s].data_ptr(), l + 1, setup.out[l + 1].data_ptr())
+
+    def timed(inst, schedule):
+        setup.reset(inst)
+        main, side = torch.cuda.Stream(), torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(main):
+            with torch.cuda.graph(g, stream=main):
+                for s in range(K):
+                    schedule(inst, s, main.cuda_stream, side.cuda_stream)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(2):
+            setup.reset(inst)
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            best = dt if best is None else min(best, dt)
+        assert inst.status() == 0
+        return best
+
+    t_serial = timed(setup.io, serial)
+    t_pref = timed(setup.io, prefetched)
+    t_noio = timed(setup.noio, serial)
+    hidden = 1.0 - (t_pref - t_noio) / (t_serial - t_noio) if t_serial > t_noio else None
+    return {"metric": "layer-wise prefetch: hidden fraction of the miss overhead",
+            "value": round(hidden, 4) if hidden is not None else None, "unit": "fraction",
+            "workload": cfg.name, "steps": K, "layers": cfg.layers,
+            "layer_compute_us": round(cyc * us_per_cycle, 2),
+            "ms_per_step": {"serial": round(t_serial / K * 1e3, 4),
+                            "prefetch": round(t_pref / K * 1e3, 4),
+                            "no_io": round(t_noio / K * 1e3, 4)},
+            "miss_overhead_us_per_step": {"serial": round((t_serial - t_noio) / K * 1e6, 1),
+                                          "prefetch": round((t_pref - t_noio) / K * 1e6, 1)},
+            "mode": "one HIP graph per schedule, best of 2 replays from a cold cache"}
+
+
+def cpu_baseline(setup, steps, threads=1):
+    """The CPU oracle (plain C) on the same trace and host rows, repeated from
+    a cold state until at least 3 s of wall time are measured.  With
+    threads > 1 the independent streams are spread over that many threads
+    (the C oracle runs without the Python lock)."""
+    from concurrent.futures import ThreadPoolExecutor
     from tests.harness import OracleRun
     cfg = setup.cfg
     streams = [(b, l) for b in range(cfg.B) for l in range(cfg.layers)]
     host_of = lambda b, l: setup.hosts[(b, l)][1]
-    elapsed, entries, reps = 0.0, 0, 0
-    while elapsed < 3.0 and reps < 50:
-        run = OracleRun(cfg, streams, host_of=host_of)
-        t0 = time.perf_counter()
+    groups = [streams[i::threads] for i in range(threads)]
+
+    def run_group(group):
+        run = OracleRun(cfg, group, host_of=host_of)
         for s in range(steps):
             if cfg.growth and s > 0:
                 run.append(s)
             run.step(s, setup.trace)
-        elapsed += time.perf_counter() - t0
-        entries += steps * cfg.layers * cfg.B * cfg.k
-        reps += 1
-    return {"value": entries / elapsed, "unit": "entries/s", "cores": 1, "kind": "oracle",
+
+    elapsed, entries, reps = 0.0, 0, 0
+    with ThreadPoolExecutor(threads) as pool:
+        while elapsed < 3.0 and reps < 50:
+            t0 = time.perf_counter()
+            list(pool.map(run_group, groups))
+            elapsed += time.perf_counter() - t0
+            entries += steps * cfg.layers * cfg.B * cfg.k
+            reps += 1
+    return {"value": entries / elapsed, "unit": "entries/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} x the full {steps}-step trace of all {len(streams)} streams "
-                      f"with row copies ({elapsed:.1f}s of CPU time, one thread)"}
+                      f"with row copies ({elapsed:.1f}s wall, {threads} thread(s))"}
 
 
 def main():
@@ -314,12 +406,20 @@ def main():
 
     torch.cuda.set_device(0)
     base = CONFIGS[args.config]
+    if args.steps is None:
+        args.steps = base.steps
     S = max(args.steps, args.warmup, 1)
     cfg = base.scaled(steps=S) if S != base.steps else base
     host_flags = hb.HISPARSE_HOST_NONCOHERENT if args.host_noncoherent else hb.HISPARSE_HOST_COHERENT
     setup = Setup(cfg, host_flags)
     K, W = args.steps, args.warmup
     io = setup.io
+    if args.prefetch_study:
+        try:
+            print(json.dumps(prefetch_study(setup, K, args.layer_compute_us)), flush=True)
+        finally:
+            setup.close()
+        return
     try:
         # ---- warm-up, then the timed region from a cold cache --------------
         for s in range(W):
@@ -442,12 +542,22 @@ def main():
 
             dt_io = graph_pass(io)
             dt_noio = graph_pass(setup.noio)
+            # resolve kernel alone, copies suppressed: eager launches, HIP events
+            setup.reset(setup.noio)
+            hb.hisparse_set_timing(setup.noio.h, True)
+            for s in range(K):
+                setup.step(setup.noio, s)
+            t_noio = hb.hisparse_get_timing(setup.noio.h)
+            hb.hisparse_set_timing(setup.noio.h, False)
+            noio_kernel_us = t_noio["resolve_ms"] / max(1, t_noio["resolve_launches"]) * 1e3
             per_call_us = dt_noio / (K * cfg.layers) * 1e6
             budget_us = DECODE_STEP_BUDGET_US / BUDGET_LAYERS * 0.05
             result["graph_replay"] = {"entries_per_s": round(entries / dt_io, 1),
                                       "ms_per_step": round(dt_io / K * 1e3, 4),
                                       "mode": "one HIP graph of all steps, best of 3"}
             result["no_io"] = {"us_per_layer_call": round(per_call_us, 3),
+                               "resolve_kernel_us": round(noio_kernel_us, 3),
+                               "includes_append_launch": bool(cfg.growth),
                                "target_us": budget_us,
                                "frac_of_decode_step_budget": round(
                                    per_call_us / (DECODE_STEP_BUDGET_US / BUDGET_LAYERS), 5),
@@ -463,6 +573,8 @@ def main():
                 result["roofline"]["frac_of_measured"] = round(fetch_gbps / lp["measured_peak_GBps"], 4)
             if not args.no_cpu_baseline:
                 result["cpu_baseline"] = cpu_baseline(setup, K)
+                result["cpu_baseline_threads"] = cpu_baseline(
+                    setup, K, threads=min(cfg.streams, len(os.sched_getaffinity(0))))
     finally:
         setup.close()
     print(json.dumps(result), flush=True)

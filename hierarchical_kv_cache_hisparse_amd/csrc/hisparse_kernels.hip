@@ -616,9 +616,12 @@ __global__ void __launch_bounds__(256) probe_host_read_kernel(const u32x4* __res
 // Launchers
 // ---------------------------------------------------------------------------
 ResolveShape resolve_shape(int k, int C, bool debug_validate) {
+  // Fewest items per thread that fit 1024 threads; then the fewest 64-lane
+  // waves that cover max(k, C) with that many items each.
   const int n = k > C ? k : C;
   ResolveShape s{0, 0, 0};
-  for (int items = 1; items <= kMaxItems; items *= 2) {
+  static const int kItems[] = {1, 2, 3, 4, 6, 8, 12, 16};
+  for (int items : kItems) {
     int threads = (n + items - 1) / items;
     threads = ((threads + 63) / 64) * 64;
     if (threads <= kMaxThreads) {
@@ -640,26 +643,20 @@ hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const i
   const ResolveShape sh = resolve_shape(v.k, v.C, (v.flags & HISPARSE_DEBUG_VALIDATE) != 0);
   const dim3 grid(v.B), block(sh.threads);
   switch (sh.items) {
-    case 1:
-      hipLaunchKernelGGL(resolve_kernel<1>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len,
-                         out, sel_copy);
-      break;
-    case 2:
-      hipLaunchKernelGGL(resolve_kernel<2>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len,
-                         out, sel_copy);
-      break;
-    case 4:
-      hipLaunchKernelGGL(resolve_kernel<4>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len,
-                         out, sel_copy);
-      break;
-    case 8:
-      hipLaunchKernelGGL(resolve_kernel<8>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len,
-                         out, sel_copy);
-      break;
-    case 16:
-      hipLaunchKernelGGL(resolve_kernel<16>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len,
-                         out, sel_copy);
-      break;
+#define HSP_RESOLVE_CASE(N)                                                                     \
+  case N:                                                                                       \
+    hipLaunchKernelGGL(resolve_kernel<N>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len, \
+                       out, sel_copy);                                                          \
+    break;
+    HSP_RESOLVE_CASE(1)
+    HSP_RESOLVE_CASE(2)
+    HSP_RESOLVE_CASE(3)
+    HSP_RESOLVE_CASE(4)
+    HSP_RESOLVE_CASE(6)
+    HSP_RESOLVE_CASE(8)
+    HSP_RESOLVE_CASE(12)
+    HSP_RESOLVE_CASE(16)
+#undef HSP_RESOLVE_CASE
     default:
       return hipErrorInvalidValue;
   }

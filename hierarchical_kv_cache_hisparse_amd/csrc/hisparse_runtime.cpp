@@ -124,7 +124,7 @@ namespace {
 int fold_timing(hisparse* h) {
   for (size_t i = 0; i < h->pool_used; ++i) {
     TimedCall& c = h->pool[i];
-    HIP_TRY(hipEventSynchronize(c.e2));
+    HIP_TRY(hipEventSynchronize(c.fetched ? c.e2 : c.e1));
     float ms = 0.f;
     HIP_TRY(hipEventElapsedTime(&ms, c.e0, c.e1));
     h->totals.resolve_ms += ms;
@@ -161,8 +161,10 @@ int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_
   }
   HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy));
   if (tc) HIP_TRY(hipEventRecord(tc->e1, s));
-  if (io && !h->view.fuse_fetch) HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
-  if (tc) HIP_TRY(hipEventRecord(tc->e2, s));
+  if (io && !h->view.fuse_fetch) {
+    HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
+    if (tc) HIP_TRY(hipEventRecord(tc->e2, s));
+  }
   return HISPARSE_OK;
 }
 
