@@ -57,6 +57,9 @@ def parse_args():
                          "with a fixed-duration stand-in for each layer's compute")
     ap.add_argument("--layer-compute-us", type=float, default=312.5,
                     help="stand-in compute per layer for --prefetch-study (20 ms / 64 layers)")
+    ap.add_argument("--mla-attention", action="store_true",
+                    help="time sparse MLA decode attention over the slot map (one layer)")
+    ap.add_argument("--heads", type=int, default=16, help="query heads for --mla-attention")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="summarize rocprofv3 CSV output in DIR into profiles/ and exit")
     ap.add_argument("--label", help="summary name (with --summarize-rocprof)")
@@ -194,7 +197,8 @@ def kernel_source_sha():
 
 
 def short_kernel_name(name):
-    for key in ("resolve_kernel", "fetch_kernel", "probe_host_read_kernel", "init_kernel",
+    for key in ("mla_decode_kernel", "mla_combine_kernel", "resolve_kernel", "fetch_kernel",
+                "probe_host_read_kernel", "init_kernel",
                 "load_window_kernel", "append_kernel", "prefetch_join_kernel"):
         if key in name:
             return key
@@ -359,6 +363,48 @@ def prefetch_study(setup, K, compute_us):
             "mode": "one HIP graph per schedule, best of 2 replays from a cold cache"}
 
 
+def mla_study(setup, K, H):
+    """Sparse MLA decode attention over the slot map of layer 0, after each of
+    K resolve steps; timed with torch events on the launching stream.
+
+    Algorithmic bytes per call: the attended rows (B * k * T * 1152), the
+    queries, outputs and lse; FLOPs: 2 * B * H * k * T * (576 + 512)."""
+    torch, hb, cfg = setup.torch, setup.hb, setup.cfg
+    from workload.rows import make_queries
+    io = setup.io
+    T = cfg.row_bytes // 1152
+    ws = torch.empty(hb.hisparse_mla_workspace_bytes(io.h, H), dtype=torch.uint8, device="cuda:0")
+    q = torch.from_numpy(make_queries(cfg.B, H, 3000 + cfg.data_seed, 0)).to("cuda:0")
+    out = torch.empty((cfg.B, H, 512), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((cfg.B, H), dtype=torch.float32, device="cuda:0")
+    scale = 1.0 / np.sqrt(576.0)
+    stream = torch.cuda.current_stream().cuda_stream
+    setup.reset(io)
+    times = []
+    for s in range(K):
+        setup.step(io, s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        hb.hisparse_sparse_mla_decode(io.h, stream, 0, q.data_ptr(), setup.out[0].data_ptr(), H,
+                                      scale, ws.data_ptr(), out.data_ptr(), lse.data_ptr())
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(times[1:] if len(times) > 1 else times))
+    n_tok = cfg.k * T
+    byts = cfg.B * n_tok * 1152 + cfg.B * H * (1152 + 512 * 4 + 4)
+    flops = 2.0 * cfg.B * H * n_tok * (576 + 512)
+    return {"metric": "sparse MLA decode attention over the slot map", "value": round(us, 3),
+            "unit": "us per layer call", "higher_is_better": False, "workload": cfg.name,
+            "requests": cfg.B, "heads": H, "attended_rows_per_request": n_tok,
+            "roofline": {"bound": "hbm", "achieved": round(byts / us / 1e3, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(byts / us / 1e3 / HBM_PEAK_GBPS, 4),
+                         "per_launch_bytes": byts},
+            "mfma": {"achieved_TFLOPs": round(flops / us / 1e6, 2), "peak_TFLOPs": 2500.0,
+                     "frac": round(flops / us / 1e6 / 2500.0, 5)},
+            "timing": "torch events around each launch, median of steps 1.."}
+
+
 def cpu_baseline(setup, steps, threads=1):
     """The CPU oracle (plain C) on the same trace and host rows, repeated from
     a cold state until at least 3 s of wall time are measured.  With
@@ -414,6 +460,12 @@ def main():
     setup = Setup(cfg, host_flags)
     K, W = args.steps, args.warmup
     io = setup.io
+    if args.mla_attention:
+        try:
+            print(json.dumps(mla_study(setup, K, args.heads)), flush=True)
+        finally:
+            setup.close()
+        return
     if args.prefetch_study:
         try:
             print(json.dumps(prefetch_study(setup, K, args.layer_compute_us)), flush=True)

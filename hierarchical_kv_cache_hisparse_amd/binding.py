@@ -109,6 +109,8 @@ def library():
             "hisparse_set_timing": [P, ctypes.c_int],
             "hisparse_get_timing": [P, P],
             "hisparse_probe_host_read": [P, P, P, SZ, I32],
+            "hisparse_mla_workspace_bytes": [P, I32, P],
+            "hisparse_sparse_mla_decode": [P, P, I32, P, P, I32, ctypes.c_float, P, P, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -225,3 +227,18 @@ def hisparse_strerror(code: int) -> str:
 
 def hisparse_last_error() -> str:
     return library().hisparse_last_error().decode(errors="replace")
+
+
+def hisparse_mla_workspace_bytes(h, num_heads: int) -> int:
+    n = ctypes.c_size_t()
+    _check(library().hisparse_mla_workspace_bytes(h, num_heads, ctypes.byref(n)),
+           "hisparse_mla_workspace_bytes")
+    return n.value
+
+
+def hisparse_sparse_mla_decode(h, stream: int, layer: int, q: int, out_slot: int,
+                               num_heads: int, scale: float, workspace: int, out: int,
+                               lse: int) -> None:
+    _check(library().hisparse_sparse_mla_decode(h, stream, layer, q, out_slot, num_heads,
+                                                scale, workspace, out, lse),
+           "hisparse_sparse_mla_decode")

@@ -474,6 +474,83 @@ int hisparse_probe_host_read(hipStream_t stream, const void* host, void* device,
   return HISPARSE_OK;
 }
 
+namespace {
+struct MlaWorkspace {
+  size_t part, ml, total;
+};
+MlaWorkspace mla_workspace(const MlaShape& sh) {
+  MlaWorkspace w{};
+  w.part = 0;
+  w.ml = align256(sizeof(float) * sh.part_floats);
+  w.total = w.ml + align256(sizeof(float) * sh.ml_floats);
+  return w;
+}
+int check_mla(const hisparse* h, int32_t num_heads) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  if (num_heads < kMlaHB || num_heads % kMlaHB != 0 || num_heads > 4096)
+    return fail(HISPARSE_ERR_INVALID_ARG, "num_heads must be a positive multiple of %d (<= 4096)",
+                kMlaHB);
+  if (h->cfg.row_bytes % (2 * kMlaDqk) != 0)
+    return fail(HISPARSE_ERR_UNSUPPORTED,
+                "sparse MLA attention needs rows of whole 576-value bf16 token rows "
+                "(row_bytes %d is not a multiple of %d)", h->cfg.row_bytes, 2 * kMlaDqk);
+  const int64_t n_tok = (int64_t)h->cfg.top_k * (h->cfg.row_bytes / (2 * kMlaDqk));
+  if (n_tok >= (int64_t(1) << 30)) return fail(HISPARSE_ERR_UNSUPPORTED, "too many token rows");
+  return HISPARSE_OK;
+}
+}  // namespace
+
+int hisparse_mla_workspace_bytes(hisparse_t h, int32_t num_heads, size_t* bytes) {
+  int rc = check_mla(h, num_heads);
+  if (rc) return rc;
+  if (!bytes) return fail(HISPARSE_ERR_INVALID_ARG, "bytes is NULL");
+  const MlaShape sh = mla_shape(h->cfg.num_requests, num_heads, h->cfg.top_k,
+                                h->cfg.row_bytes / (2 * kMlaDqk));
+  *bytes = mla_workspace(sh).total;
+  return HISPARSE_OK;
+}
+
+int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, const void* q,
+                               const int32_t* out_slot, int32_t num_heads, float scale,
+                               void* workspace, float* out, float* lse) {
+  int rc = check_mla(h, num_heads);
+  if (rc) return rc;
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
+  if (!q || !out_slot || !workspace || !out || !lse)
+    return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(HISPARSE_ERR_INVALID_ARG, "q must be 16-byte and workspace 256-byte aligned");
+  const int B = h->cfg.num_requests;
+  const int T = h->cfg.row_bytes / (2 * kMlaDqk);
+  const MlaShape sh = mla_shape(B, num_heads, h->cfg.top_k, T);
+  const MlaWorkspace ws = mla_workspace(sh);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  MlaArgs a{};
+  const int64_t stream_bytes =
+      ((int64_t)h->cfg.cache_slots + h->cfg.resident_window) * h->cfg.row_bytes;
+  a.cache = h->view.cache + (int64_t)layer * B * stream_bytes;
+  a.stream_bytes = stream_bytes;
+  a.row_bytes = h->cfg.row_bytes;
+  a.slots_total = h->cfg.cache_slots + h->cfg.resident_window;
+  a.T = T;
+  a.k = h->cfg.top_k;
+  a.B = B;
+  a.H = num_heads;
+  a.HBn = sh.HBn;
+  a.S = sh.S;
+  a.rows_per_split = sh.rows_per_split;
+  a.scale = scale;
+  a.q = static_cast<const __bf16*>(q);
+  a.slots = out_slot;
+  a.part = reinterpret_cast<float*>(w + ws.part);
+  a.part_ml = reinterpret_cast<float*>(w + ws.ml);
+  a.out = out;
+  a.lse = lse;
+  HIP_TRY(launch_mla(a, stream, sh.lds_bytes, B * sh.HBn * sh.S));
+  return HISPARSE_OK;
+}
+
 const char* hisparse_strerror(int code) {
   switch (code) {
     case HISPARSE_OK: return "success";

@@ -249,6 +249,38 @@ int hisparse_get_timing(hisparse_t h, hisparse_timing* out);
 int hisparse_probe_host_read(hipStream_t stream, const void* host, void* device, size_t bytes,
                              int32_t workgroups);
 
+/* ---- sparse MLA decode attention over the slot map ----------------------
+ * The step the slot map exists for: attention of every request's query heads
+ * over the rows its slot map points at, read from the HBM slot cache.  Only
+ * placement changes, so the result equals attention over the same positions
+ * of the full host history [P3 Abstract]; the method sits under sparse MLA
+ * decoding [P2 Timeline; P1 Timeline].
+ *
+ * Rows are sparse-MLA latent rows: 576 bf16 = 512 latent values (keys and
+ * values) + 64 rope values (keys only); a slot holds row_bytes / 1152 token
+ * rows (16 for 16-token pages), all of which are attended.  For request b,
+ * head h:  score_i = scale * q[b,h,:] . row_i[:576];  out[b,h,:] =
+ * sum_i softmax(score)_i * row_i[:512];  lse[b,h] = log sum_i exp(score_i)
+ * (-inf and out = 0 when every entry is padding).  fp32 accumulation; the
+ * softmax weights enter the value product with ~24 significant bits.
+ *
+ * hisparse_mla_workspace_bytes: size of the caller-owned device workspace
+ *   (per-split partial results) for num_heads, a multiple of 16.  Host only;
+ *   the workspace needs no initialisation.
+ * hisparse_sparse_mla_decode (async on `stream`, graph-capturable; two
+ *   launches: the split attention, then the merge of the splits):
+ *   q:        device bf16 [B, num_heads, 576], 16-byte aligned;
+ *   out_slot: device int32 [B, k], as written by hisparse_resolve for `layer`;
+ *   workspace: 256-byte aligned, hisparse_mla_workspace_bytes bytes;
+ *   out:      device fp32 [B, num_heads, 512];  lse: device fp32 [B, num_heads].
+ * Errors: INVALID_ARG (NULL, misaligned, bad layer or head count),
+ * UNSUPPORTED (row_bytes not a multiple of 1152), HIP.  Launches sharing one
+ * workspace must be ordered (same stream). */
+int hisparse_mla_workspace_bytes(hisparse_t h, int32_t num_heads, size_t* bytes);
+int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, const void* q,
+                               const int32_t* out_slot, int32_t num_heads, float scale,
+                               void* workspace, float* out, float* lse);
+
 /* Text for a return code, and the last failure of the calling thread. */
 const char* hisparse_strerror(int code);
 const char* hisparse_last_error(void);

@@ -52,3 +52,21 @@ def masked_dense_attention(q: np.ndarray, all_rows: np.ndarray, mask: np.ndarray
     """Attention over the full history in position order, with the positions
     outside ``mask`` excluded (weight exactly 0)."""
     return mla_decode_attention(q, all_rows[mask], scale)
+
+
+def mla_decode_attention_lse(q: np.ndarray, rows: np.ndarray, scale: float):
+    """As mla_decode_attention, also returning lse[h] = log sum_i exp(score[h, i]).
+    With no rows the output is 0 and lse is -inf."""
+    H = q.shape[0]
+    out = np.zeros((H, D_LATENT), np.float64)
+    lse = np.full(H, -np.inf)
+    if rows.shape[0] == 0:
+        return out, lse
+    for h in range(H):
+        score = scale * (rows * q[h][None, :]).sum(axis=1)
+        m = score.max()
+        e = np.exp(score - m)
+        z = e.sum()
+        out[h] = ((e / z)[:, None] * rows[:, :D_LATENT]).sum(axis=0)
+        lse[h] = m + np.log(z)
+    return out, lse

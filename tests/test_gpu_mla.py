@@ -1,0 +1,166 @@
+"""GPU sparse-MLA decode attention over the slot map, against the float64
+oracle attention over the *host* rows at the selected positions.
+
+This is the exactness claim of the method on the GPU path: resolution only
+changes where rows live, so attention through the slot map must equal
+attention over the full history ("HiSparse: Scaling Sparse-Attention Decoding
+with Hierarchical KV Cache Management", Abstract).
+
+Tolerance (derived from the arithmetic, stated once): q and the rows are
+exact bf16; each product is exact in fp32 and the 576-term score sums in fp32
+(error ~ sqrt(576) * 2^-24 * |q||k| ~ 1e-6 after the 1/sqrt(576) scale); the
+softmax weights enter the value product as bf16 hi + lo (~2^-16 relative);
+the output is a weighted mean of N(0,1) values, so its absolute error stays
+below ~2^-16 * E|v| ~ 1.2e-5.  We allow 5e-5 absolute on out and 2e-5 on lse.
+"""
+import numpy as np
+import pytest
+
+from workload import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+OUT_ATOL = 5e-5
+LSE_ATOL = 2e-5
+
+
+def _reference(cfg, host, sel, q_bytes, scale):
+    """float64 oracle over the host rows at the selected positions."""
+    from oracle.attention import bf16_to_f64, mla_decode_attention_lse
+    T = cfg.row_bytes // 1152
+    pos = sel[sel >= 0]
+    rows = host[pos].reshape(-1, 1152) if T > 1 else host[pos]
+    q = bf16_to_f64(q_bytes)
+    return mla_decode_attention_lse(q, bf16_to_f64(rows), scale)
+
+
+class Attn:
+    def __init__(self, run, H):
+        import torch
+        from hierarchical_kv_cache_hisparse_amd import binding as hb
+        self.run, self.H, self.hb, self.torch = run, H, hb, torch
+        cfg = run.cfg
+        ws = hb.hisparse_mla_workspace_bytes(run.gpu.h, H)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")   # needs no initialisation
+        self.out = torch.empty((cfg.B, H, 512), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((cfg.B, H), dtype=torch.float32, device="cuda")
+        from workload.rows import make_queries
+        self.q_bytes = {l: make_queries(cfg.B, H, 3000 + cfg.data_seed, l) for l in range(cfg.layers)}
+        self.q = {l: torch.from_numpy(self.q_bytes[l]).to("cuda") for l in self.q_bytes}
+        self.scale = 1.0 / np.sqrt(576.0)
+
+    def launch(self, layer, out_slot):
+        self.hb.hisparse_sparse_mla_decode(
+            self.run.gpu.h, self.torch.cuda.current_stream().cuda_stream, layer,
+            self.q[layer].data_ptr(), out_slot.data_ptr(), self.H, self.scale,
+            self.ws.data_ptr(), self.out.data_ptr(), self.lse.data_ptr())
+
+    def check(self, s, layer, requests=None):
+        cfg = self.run.cfg
+        out = self.out.cpu().numpy()
+        lse = self.lse.cpu().numpy()
+        worst = 0.0
+        for b in (range(cfg.B) if requests is None else requests):
+            sel = self.run.trace[s, layer, b]
+            ref, ref_lse = _reference(cfg, self.run.gpu.host(b, layer), sel,
+                                      self.q_bytes[layer][b], self.scale)
+            err = np.abs(out[b] - ref).max()
+            worst = max(worst, err)
+            assert err <= OUT_ATOL, f"step {s} layer {layer} request {b}: out error {err}"
+            np.testing.assert_allclose(lse[b], ref_lse, atol=LSE_ATOL, rtol=0,
+                                       err_msg=f"lse step {s} layer {layer} request {b}")
+        return worst
+
+
+def _run(cfg, H, steps=None, requests=None):
+    import torch
+    from tests.gpu_harness import LockstepRun
+    run = LockstepRun(cfg, oracle_streams=[])
+    attn = Attn(run, H)
+    worst = 0.0
+    try:
+        for s in range(cfg.steps if steps is None else steps):
+            if s > 0 and cfg.growth:
+                run.append_rows(s)
+            run.gpu_step(s)
+            for l in range(cfg.layers):
+                attn.launch(l, run.out_dev[l])
+                torch.cuda.synchronize()
+                worst = max(worst, attn.check(s, l, requests))
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+    print(f"[mla] max |out - oracle| = {worst:.3e}")
+
+
+@pytest.mark.parametrize("H", [16, 48])
+def test_attention_over_token_slots(H):
+    cfg = CONFIGS[2].scaled(B=3, L0=8192, C=1500, k=700, steps=3)
+    _run(cfg, H)
+
+
+def test_attention_over_page_slots():
+    cfg = CONFIGS[5].scaled(B=2, layers=2, L0=3000, C=64, k=40, steps=3)
+    _run(cfg, 16)
+
+
+def test_attention_full_shared_selection_step():
+    """The 16-request, 2048-selection shape of the shared-selection workload
+    (one layer), 128 heads, sampled requests."""
+    cfg = CONFIGS[4].scaled(layers=1, steps=2)
+    _run(cfg, 128, requests=[0, 7, 15])
+
+
+def test_attention_skips_padding_and_empty_rows():
+    import torch
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    from tests.gpu_harness import LockstepRun
+    cfg = CONFIGS[2].scaled(B=3, L0=4000, C=512, k=200, steps=1)
+    run = LockstepRun(cfg, oracle_streams=[])
+    attn = Attn(run, 16)
+    try:
+        trace = run.trace.copy()
+        trace[0, 0, 1, ::3] = -1          # request 1: a third padding
+        trace[0, 0, 2, :] = -1            # request 2: nothing selected
+        run.trace = trace
+        sel = torch.from_numpy(trace[0, 0]).cuda()
+        hb.hisparse_resolve(run.gpu.h, run.gpu.stream, sel.data_ptr(), run.ctx_dev[0].data_ptr(),
+                            0, run.out_dev[0].data_ptr())
+        attn.launch(0, run.out_dev[0])
+        torch.cuda.synchronize()
+        attn.check(0, 0, requests=[0, 1])
+        assert (attn.out[2] == 0).all() and torch.isinf(attn.lse[2]).all()
+        assert (attn.lse[2] < 0).all()
+    finally:
+        run.close()
+
+
+def test_attention_graph_replays_are_bit_reproducible():
+    """Captured once (split attention + merge), replayed several times with
+    eager work in between: every replay equals the eager launch bit for bit."""
+    import torch
+    from tests.gpu_harness import LockstepRun
+    cfg = CONFIGS[2].scaled(B=4, L0=6000, C=1024, k=512, steps=1)
+    run = LockstepRun(cfg, oracle_streams=[])
+    attn = Attn(run, 32)
+    try:
+        run.gpu_step(0)
+        torch.cuda.synchronize()
+        attn.launch(0, run.out_dev[0])
+        torch.cuda.synchronize()
+        eager = attn.out.clone()
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                attn.launch(0, run.out_dev[0])
+        torch.cuda.synchronize()
+        for _ in range(4):
+            attn.out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(attn.out, eager)
+        attn.check(0, 0)
+    finally:
+        run.close()

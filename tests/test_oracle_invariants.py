@@ -111,3 +111,24 @@ def test_attention_check_detects_a_wrong_row():
     bad = rows.copy()
     bad[10] = rng.standard_normal(576)
     assert not np.allclose(a, mla_decode_attention(q, bad, 0.05), rtol=1e-9)
+
+
+def test_attention_lse_closed_forms():
+    """lse of one row is its score; of n identical rows, score + log n; the
+    output of identical rows is the row's latent part; no rows -> 0, -inf."""
+    from oracle.attention import mla_decode_attention_lse
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((3, 576))
+    row = rng.standard_normal(576)
+    out, lse = mla_decode_attention_lse(q, row[None, :], 0.1)
+    np.testing.assert_allclose(lse, 0.1 * q @ row, rtol=1e-13)
+    np.testing.assert_allclose(out, np.repeat(row[None, :512], 3, axis=0), rtol=1e-13)
+    out, lse = mla_decode_attention_lse(q, np.repeat(row[None, :], 7, axis=0), 0.1)
+    np.testing.assert_allclose(lse, 0.1 * q @ row + np.log(7), rtol=1e-13)
+    out, lse = mla_decode_attention_lse(q, np.zeros((0, 576)), 0.1)
+    assert (out == 0).all() and np.isneginf(lse).all()
+    # agrees with the plain version
+    rows = rng.standard_normal((50, 576))
+    o1 = mla_decode_attention(q, rows, 0.05)
+    o2, _ = mla_decode_attention_lse(q, rows, 0.05)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12)

@@ -76,3 +76,13 @@ def bf16_bytes_to_f64(raw: np.ndarray) -> np.ndarray:
     """Decode little-endian bf16 bytes to float64 (exact)."""
     u16 = np.ascontiguousarray(raw).view(np.uint16)
     return (u16.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def make_queries(B: int, H: int, seed: int, layer: int) -> np.ndarray:
+    """Seeded query heads for sparse-MLA decode: bf16 bytes uint8 [B, H, 1152]
+    (576 values per head, N(0,1) like the rows, from their own seed)."""
+    out = np.empty((B, H, 1152), np.uint8)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = make_row(576, h, seed, b, layer)
+    return out
