@@ -57,6 +57,9 @@ def parse_args():
                          "with a fixed-duration stand-in for each layer's compute")
     ap.add_argument("--layer-compute-us", type=float, default=312.5,
                     help="stand-in compute per layer for --prefetch-study (20 ms / 64 layers)")
+    ap.add_argument("--layer-compute", choices=("busy", "attention"), default="busy",
+                    help="--prefetch-study per-layer compute: the calibrated busy kernel, or the "
+                         "sparse MLA decode attention over the layer's slot map (--heads)")
     ap.add_argument("--mla-attention", action="store_true",
                     help="time sparse MLA decode attention over the slot map (one layer)")
     ap.add_argument("--heads", type=int, default=16, help="query heads for --mla-attention")
@@ -286,7 +289,7 @@ def committed_traffic(kernel, cfg_name, mode):
     return vals
 
 
-def prefetch_study(setup, K, compute_us):
+def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
     """Exact layer-wise prefetch on a shared-selection workload.
 
     Per layer a stand-in compute kernel (torch's fixed-cycle busy kernel,
@@ -308,12 +311,30 @@ def prefetch_study(setup, K, compute_us):
         ev0.record(); torch.cuda._sleep(cycles); ev1.record(); torch.cuda.synchronize()
     us_per_cycle = ev0.elapsed_time(ev1) * 1e3 / cycles
     cyc = max(1, int(round(compute_us / us_per_cycle)))
+    attn = {}
+    if compute == "attention":
+        from workload.rows import make_queries
+        for inst in (setup.io, setup.noio):
+            attn[id(inst)] = torch.empty(hb.hisparse_mla_workspace_bytes(inst.h, heads),
+                                         dtype=torch.uint8, device="cuda:0")
+        qs = [torch.from_numpy(make_queries(cfg.B, heads, 3000 + cfg.data_seed, l)).to("cuda:0")
+              for l in range(cfg.layers)]
+        a_out = torch.empty((cfg.B, heads, 512), dtype=torch.float32, device="cuda:0")
+        a_lse = torch.empty((cfg.B, heads), dtype=torch.float32, device="cuda:0")
+
+    def layer_compute(inst, l, ms):
+        if compute == "attention":
+            hb.hisparse_sparse_mla_decode(inst.h, ms, l, qs[l].data_ptr(), setup.out[l].data_ptr(),
+                                          heads, 1.0 / np.sqrt(576.0), attn[id(inst)].data_ptr(),
+                                          a_out.data_ptr(), a_lse.data_ptr())
+        else:
+            torch.cuda._sleep(cyc)
 
     def serial(inst, s, ms, ss):
         for l in range(cfg.layers):
             hb.hisparse_resolve(inst.h, ms, setup.sel[s, l].data_ptr(), setup.ctx[s].data_ptr(), l,
                                 setup.out[l].data_ptr())
-            torch.cuda._sleep(cyc)
+            layer_compute(inst, l, ms)
 
     def prefetched(inst, s, ms, ss):
         hb.hisparse_resolve(inst.h, ms, setup.sel[s, 0].data_ptr(), setup.ctx[s].data_ptr(), 0,
@@ -322,7 +343,7 @@ def prefetch_study(setup, K, compute_us):
             if l + 1 < cfg.layers:
                 hb.hisparse_prefetch(inst.h, ms, ss, setup.sel[s, l + 1].data_ptr(),
                                      setup.ctx[s].data_ptr(), l + 1)
-            torch.cuda._sleep(cyc)
+            layer_compute(inst, l, ms)
             if l + 1 < cfg.layers:
                 hb.hisparse_resolve(inst.h, ms, setup.sel[s, l + 1].data_ptr(),
                                     setup.ctx[s].data_ptr(), l + 1, setup.out[l + 1].data_ptr())
@@ -354,7 +375,8 @@ def prefetch_study(setup, K, compute_us):
     return {"metric": "layer-wise prefetch: hidden fraction of the miss overhead",
             "value": round(hidden, 4) if hidden is not None else None, "unit": "fraction",
             "workload": cfg.name, "steps": K, "layers": cfg.layers,
-            "layer_compute_us": round(cyc * us_per_cycle, 2),
+            "layer_compute": (f"sparse MLA attention, {heads} heads" if compute == "attention"
+                              else f"busy kernel, {round(cyc * us_per_cycle, 2)} us"),
             "ms_per_step": {"serial": round(t_serial / K * 1e3, 4),
                             "prefetch": round(t_pref / K * 1e3, 4),
                             "no_io": round(t_noio / K * 1e3, 4)},
@@ -391,6 +413,22 @@ def mla_study(setup, K, H):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) * 1e3)
     us = float(np.median(times[1:] if len(times) > 1 else times))
+    # the float64 oracle attention on the host, over the host rows at the last
+    # step's selections, for as many requests as fit ~10 s (at least one)
+    from oracle.attention import bf16_to_f64, mla_decode_attention_lse
+    q_np = make_queries(cfg.B, H, 3000 + cfg.data_seed, 0)
+    t_cpu, n_cpu = 0.0, 0
+    for b in range(cfg.B):
+        sel = setup.trace[K - 1, 0, b]
+        host = setup.hosts[(b, 0)][1]
+        rows = host[sel[sel >= 0]].reshape(-1, 1152)
+        t0 = time.perf_counter()
+        mla_decode_attention_lse(bf16_to_f64(q_np[b]), bf16_to_f64(rows), scale)
+        t_cpu += time.perf_counter() - t0
+        n_cpu += 1
+        if t_cpu > 10.0:
+            break
+    cpu_us_per_call = t_cpu / n_cpu * cfg.B * 1e6
     n_tok = cfg.k * T
     byts = cfg.B * n_tok * 1152 + cfg.B * H * (1152 + 512 * 4 + 4)
     flops = 2.0 * cfg.B * H * n_tok * (576 + 512)
@@ -402,7 +440,11 @@ def mla_study(setup, K, H):
                          "per_launch_bytes": byts},
             "mfma": {"achieved_TFLOPs": round(flops / us / 1e6, 2), "peak_TFLOPs": 2500.0,
                      "frac": round(flops / us / 1e6 / 2500.0, 5)},
-            "timing": "torch events around each launch, median of steps 1.."}
+            "timing": "torch events around each launch, median of steps 1..",
+            "cpu_baseline": {"value": round(cpu_us_per_call, 1), "unit": "us per layer call",
+                             "cores": 1, "kind": "oracle",
+                             "sample": f"float64 numpy oracle on {n_cpu} of {cfg.B} requests of the "
+                                       f"last step, scaled to all requests"}}
 
 
 def cpu_baseline(setup, steps, threads=1):
@@ -468,7 +510,8 @@ def main():
         return
     if args.prefetch_study:
         try:
-            print(json.dumps(prefetch_study(setup, K, args.layer_compute_us)), flush=True)
+            print(json.dumps(prefetch_study(setup, K, args.layer_compute_us, args.layer_compute,
+                                            args.heads)), flush=True)
         finally:
             setup.close()
         return
