@@ -144,3 +144,38 @@ class OracleStream:
         self.t[:] = snap["t"]
         if self.slots is not None:
             self.slots[:] = snap["slots"]
+
+
+
+def resolve_multi(stream: OracleStream, sel, ctx: int, no_io: bool = False) -> StepResult:
+    """Selections of several query tokens of one request, resolved in one step.
+
+    Reading: the pages list multi-token prediction only as a feature the
+    method stays compatible with ("Hybrid HiSparse", Timeline).  Every query
+    token of the step attends through the same cache, so the cache has to hold
+    the union of their selections at once; the step is therefore one
+    resolution of that union, which is one clock tick for the stream.  The
+    union is written in first-occurrence order over the entries (query-major,
+    then index) and padded with -1 to the Q*k entries of the call, so that a
+    position that misses is fetched once and the j-th distinct miss takes the
+    j-th victim.  Every entry is then served by its position's slot; padding
+    stays -1.  The counters and the eviction log are those of the union row.
+    A rejected union (any entry outside [-1, ctx), or a bad ctx) serves -1
+    everywhere and leaves the stream untouched, as the single-query step does.
+
+    sel: int [Q, k].  Returns a StepResult whose `out` is int32 [Q, k].
+    """
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    if sel.ndim != 2:
+        raise ValueError("sel must be [queries, k]")
+    Q, k = sel.shape
+    flat = sel.reshape(-1).tolist()
+    union = np.full(Q * k, -1, np.int32)
+    first = {}
+    for p in flat:
+        if p != -1 and p not in first:
+            first[p] = len(first)
+            union[first[p]] = p
+    r = stream.resolve(union, ctx, no_io=no_io)
+    out = np.array([-1 if p == -1 else int(r.out[first[p]]) for p in flat], np.int32)
+    return StepResult(r.status, out.reshape(Q, k), r.log_slot, r.log_old, r.counters)

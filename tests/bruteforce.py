@@ -56,5 +56,51 @@ class BruteStream:
         self.recency = [s for s in self.recency if s not in touched] + sorted(touched)
         return out, log
 
+    def resolve_multi(self, queries, ctx):
+        """Several queries' selections in one step, entry by entry: the first
+        entry of a position classifies it (resident, hit, or a new miss in
+        the order first met); later entries of the same position reuse its
+        slot.  Victims as in `resolve`.  Returns (out per query, log,
+        (n_pad, n_res, n_hit, n_miss)) over the Q*k entries, with each
+        distinct position counted once and the rest counted as padding."""
+        width = sum(len(q) for q in queries)
+        for q in queries:
+            for p in q:
+                if p < -1 or p >= ctx:
+                    return None
+        if width > self.C:
+            return None
+        slot_of, touched, pending = {}, set(), []
+        n_res = n_hit = 0
+        for q in queries:
+            for p in q:
+                if p == -1 or p in slot_of or p in pending:
+                    continue
+                if self.R > 0 and p >= ctx - self.R:
+                    slot_of[p] = self.C + p % self.R
+                    n_res += 1
+                elif p in self.where:
+                    slot_of[p] = self.where[p]
+                    touched.add(self.where[p])
+                    n_hit += 1
+                else:
+                    pending.append(p)
+        candidates = [s for s in self.recency if s not in touched]
+        log = []
+        for j, p in enumerate(pending):
+            s = candidates[j]
+            old = self.held[s]
+            log.append((s, -1 if old is None else old))
+            if old is not None:
+                del self.where[old]
+            self.where[p] = s
+            self.held[s] = p
+            touched.add(s)
+            slot_of[p] = s
+        self.recency = [s for s in self.recency if s not in touched] + sorted(touched)
+        out = [[-1 if p == -1 else slot_of[p] for p in q] for q in queries]
+        n_distinct = len(slot_of)
+        return out, log, (width - n_distinct, n_res, n_hit, len(pending))
+
     def slot2pos(self):
         return [-1 if p is None else p for p in self.held]

@@ -11,7 +11,7 @@ import os
 
 import numpy as np
 
-from oracle.oracle import OracleStream
+from oracle.oracle import OracleStream, resolve_multi as _oracle_resolve_multi
 from tests.bruteforce import BruteStream
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -24,7 +24,18 @@ def parse_golden(name: str):
             line = line.strip()
             if not line or line.startswith("#"):
                 continue
-            if line.startswith("step"):
+            if line.startswith("mstep"):
+                ev = {}
+                for part in line.split("|"):
+                    key, *vals = part.split()
+                    if key == "log":
+                        ev[key] = [tuple(int(x) for x in v.split(":")) for v in vals]
+                    elif key in ("sel", "out"):
+                        ev[key] = [[int(x) for x in q.split()] for q in " ".join(vals).split(";")]
+                    else:
+                        ev[key] = [int(v) for v in vals]
+                events.append(("mstep", ev))
+            elif line.startswith("step"):
                 ev = {}
                 for part in line.split("|"):
                     key, *vals = part.split()
@@ -190,3 +201,74 @@ def check_validation(lib=None):
             assert (getattr(st, key) == val).all(), f"{key} changed by a rejected row"
     r = st.resolve([-1, -1], 10)
     assert r.status == 0 and r.out.tolist() == [-1, -1] and int(st.t[0]) == 2
+
+
+def check_golden_multi(name: str = "multi_query_example.txt", lib=None, resolve_multi=None):
+    """Hand-derived multi-query example: out per entry, status, eviction log,
+    union counters, slot2pos, last_use, the clock, and the slot bytes."""
+    resolve_multi = resolve_multi or _oracle_resolve_multi
+    cfg, events = parse_golden(name)
+    C, R, L = cfg["C"], cfg["R"], cfg["L"]
+    row_bytes = 16
+    host = np.zeros((L, row_bytes), np.uint8)
+    for p in range(L):
+        host[p] = (p * 5 + 3 * np.arange(row_bytes)) % 239
+    st = OracleStream(C, R, L, row_bytes, host=host, lib=lib)
+    st.seed_window(next(ev["ctx"][0] for kind, ev in events if kind == "mstep"))
+    for kind, ev in events:
+        assert kind == "mstep"
+        where = f"{name} call at t={ev['mstep'][0]}"
+        r = resolve_multi(st, np.array(ev["sel"]), ev["ctx"][0])
+        assert r.status == ev["status"][0], f"{where}: status {r.status}"
+        assert r.out.tolist() == ev["out"], f"{where}: out {r.out.tolist()} != {ev['out']}"
+        got_log = list(zip(r.log_slot.tolist(), r.log_old.tolist()))
+        assert got_log == ev["log"], f"{where}: log {got_log} != {ev['log']}"
+        c = r.counters
+        got = [c["n_pad"], c["n_res"], c["n_hit"], c["n_miss"], c["n_evict"]]
+        assert got == ev["counts"], f"{where}: counters {got} != {ev['counts']}"
+        assert st.slot2pos.tolist() == ev["slot2pos"], f"{where}: slot2pos"
+        assert st.last_use.tolist() == ev["last_use"], f"{where}: last_use"
+        assert int(st.t[0]) == ev["mstep"][0], f"{where}: clock {int(st.t[0])}"
+        for q, row in enumerate(ev["sel"]):
+            for i, p in enumerate(row):
+                if p >= 0 and r.status == 0:
+                    assert (st.slots[r.out[q, i]] == host[p]).all(), f"{where}: bytes of {p}"
+
+
+def check_bruteforce_multi(lib=None, n_traces: int = 200, seed: int = 11, resolve_multi=None):
+    """Random tiny multi-query traces (Q <= 3 queries of k <= 3 selections over
+    few positions, so the queries overlap), checked against the brute-force
+    entry-wise formulation: out per entry, eviction log, slot2pos and the
+    distinct-position counters."""
+    resolve_multi = resolve_multi or _oracle_resolve_multi
+    rng = np.random.default_rng(seed)
+    for n in range(n_traces):
+        Q = int(rng.integers(1, 4))
+        k = int(rng.integers(1, 4))
+        C = Q * k + int(rng.integers(0, 3))
+        R = int(rng.integers(0, 3))
+        L = int(rng.integers(max(k, 3), 10))
+        steps = int(rng.integers(2, 12))
+        st = OracleStream(C, R, L, 16, lib=lib)
+        br = BruteStream(C, R)
+        for s in range(steps):
+            sel = np.full((Q, k), -1, np.int32)
+            for q in range(Q):
+                n_sel = k if rng.random() < 0.8 else int(rng.integers(0, k + 1))
+                sel[q, :n_sel] = rng.choice(L, n_sel, replace=False)
+                sel[q] = rng.permutation(sel[q])
+            if rng.random() < 0.03:
+                sel[int(rng.integers(0, Q)), int(rng.integers(0, k))] = L + int(rng.integers(0, 2))
+            where = f"multi trace {n} step {s}"
+            r = resolve_multi(st, sel, L)
+            b = br.resolve_multi(sel.tolist(), L)
+            if b is None:
+                assert r.status != 0 and (r.out == -1).all(), f"{where}: invalid call accepted"
+                continue
+            assert r.status == 0, f"{where}: valid call rejected"
+            out, log, counts = b
+            assert r.out.tolist() == out, f"{where}: out {r.out.tolist()} != {out}"
+            assert list(zip(r.log_slot.tolist(), r.log_old.tolist())) == log, f"{where}: log"
+            assert st.slot2pos.tolist() == br.slot2pos(), f"{where}: slot2pos"
+            c = r.counters
+            assert (c["n_pad"], c["n_res"], c["n_hit"], c["n_miss"]) == counts, f"{where}: counters"
