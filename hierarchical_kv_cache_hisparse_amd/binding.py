@@ -101,6 +101,7 @@ def library():
             "hisparse_create": [P, P, P, P, P],
             "hisparse_destroy": [P],
             "hisparse_resolve": [P, P, P, P, I32, P],
+            "hisparse_resolve_multi": [P, P, P, I32, I32, P, I32, P],
             "hisparse_prefetch": [P, P, P, P, P, I32],
             "hisparse_load_window": [P, P, I32, P],
             "hisparse_append": [P, P, I32, P, P],
@@ -177,6 +178,12 @@ def hisparse_destroy(h) -> None:
 def hisparse_resolve(h, stream: int, sel: int, ctx_len: int, layer: int, out_slot: int) -> None:
     _check(library().hisparse_resolve(h, stream, sel, ctx_len, layer, out_slot),
            "hisparse_resolve")
+
+
+def hisparse_resolve_multi(h, stream: int, sel: int, queries: int, per_query: int, ctx_len: int,
+                           layer: int, out_slot: int) -> None:
+    _check(library().hisparse_resolve_multi(h, stream, sel, queries, per_query, ctx_len, layer,
+                                            out_slot), "hisparse_resolve_multi")
 
 
 def hisparse_prefetch(h, main_stream: int, side_stream: int, sel: int, ctx_len: int,

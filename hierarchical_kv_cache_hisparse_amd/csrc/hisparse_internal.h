@@ -84,13 +84,16 @@ inline uint32_t div_magic(uint32_t d) {
   return d <= 1 ? 0xFFFFFFFFu : (uint32_t)((uint64_t(1) << 32) / d);
 }
 
-ResolveShape resolve_shape(int k, int C, bool debug_validate);
+// multi_entries > 0: rows of that many entries from several query tokens
+// (repeated positions allowed), see hisparse_resolve_multi.
+ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries = 0);
 
 // Kernel launchers (hisparse_kernels.hip).  All are asynchronous on `s`.
 hipError_t launch_init(const StreamView& v, hipStream_t s, int layer, int request,
                        bool clear_status);
 hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const int32_t* sel,
-                          const int32_t* ctx_len, int32_t* out, int32_t* sel_copy);
+                          const int32_t* ctx_len, int32_t* out, int32_t* sel_copy,
+                          int multi_entries = 0);
 hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid_x);
 hipError_t launch_prefetch_join(const StreamView& v, hipStream_t s, const int32_t* sel,
                                 const int32_t* sel_copy, const int32_t* pf_out, int32_t* out);

@@ -38,7 +38,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-enum Cls : int { kNone = 0, kPad = 1, kRes = 2, kHit = 3, kMiss = 4, kBad = 5 };
+enum Cls : int { kNone = 0, kPad = 1, kRes = 2, kHit = 3, kMiss = 4, kBad = 5, kRepeat = 6 };
 
 struct StreamPtrs {
   int32_t* hdr;
@@ -166,12 +166,21 @@ __device__ __forceinline__ bool test_bit(const uint32_t* bm, int s) {
 // staged and the unreferenced slots counted; 3 after the victims are taken.
 // No global write happens before barrier 1, so a rejected row leaves the
 // stream untouched.
+//
+// Several query tokens per request (`ke` > 0): the row holds ke entries (the
+// queries' selections one after another) and may repeat positions.  The step
+// resolves their union once: an LDS hash keyed by position keeps each
+// position's first entry index (atomicMin; one more barrier, D), the first
+// entry is classified as usual and the later ones are set aside as repeats
+// (counted with the padding).  Misses then come in first-entry order, as in
+// the union written in first-occurrence order.  The first entries leave
+// their slot in LDS, and after barrier 3 every repeat is served that slot.
 // ---------------------------------------------------------------------------
 template <int IPT>
 __global__ void __launch_bounds__(kMaxThreads)
     resolve_kernel(StreamView v, int layer, const int32_t* __restrict__ sel_all,
                    const int32_t* __restrict__ ctx_len, int32_t* __restrict__ out_all,
-                   int32_t* __restrict__ sel_copy) {
+                   int32_t* __restrict__ sel_copy, int ke_multi) {
   extern __shared__ int lds[];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -180,12 +189,17 @@ __global__ void __launch_bounds__(kMaxThreads)
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int C = v.C, R = v.R, k = v.k;
-  const bool debug = (v.flags & HISPARSE_DEBUG_VALIDATE) != 0;
+  const bool multi = ke_multi > 0;
+  const int ke = multi ? ke_multi : k;  // entries per row (ke <= k)
+  const bool debug = !multi && (v.flags & HISPARSE_DEBUG_VALIDATE) != 0;
   const StreamPtrs st = stream_ptrs(v, layer, b);
-  const int32_t* sel = sel_all + (int64_t)b * k;
-  int32_t* out = out_all + (int64_t)b * k;
+  const int32_t* sel = sel_all + (int64_t)b * ke;
+  int32_t* out = out_all + (int64_t)b * ke;
 
   // LDS: [bitmap C bits][slot2pos C][miss pos k][miss idx k][cntA][cntB][misc 8][hash]
+  // hash: debug: H position keys; several queries: H keys, then H first-entry
+  // indices (the key words are reused for the first entries' slots once the
+  // first entries are known).
   const int nbm = (C + 31) >> 5;
   uint32_t* bitmap = (uint32_t*)lds;
   int* s2p = lds + nbm;
@@ -194,8 +208,12 @@ __global__ void __launch_bounds__(kMaxThreads)
   int* cntA = missi + k;
   int* cntB = cntA + IPT * W;
   int* misc = cntB + IPT * W;  // 0 error bits, 1 pad, 2 res, 3 hit, 4 evictions
+  const int H = multi ? (2 << (31 - __clz(2 * ke - 1)))   // power of two >= 2 ke
+                      : debug ? (2 << (31 - __clz(k)))    // power of two > k
+                              : 0;
   int* hash = misc + 8;
-  const int H = debug ? (2 << (31 - __clz(k))) : 0;  // power of two > k
+  int* first = hash + (multi ? H : 0);
+  int* eslot = hash;
 
   // ---- Phase A: independent loads; clear LDS ------------------------------
   int32_t p[IPT], o[IPT], q2[IPT], slot[IPT];
@@ -203,8 +221,8 @@ __global__ void __launch_bounds__(kMaxThreads)
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
     const int i = r * BD + tid;
-    p[r] = (i < k) ? sel[i] : -1;
-    cls[r] = (i < k) ? kPad : kNone;
+    p[r] = (i < ke) ? sel[i] : -1;
+    cls[r] = (i < ke) ? kPad : kNone;
   }
 #pragma unroll
   for (int r = 0; r < IPT; ++r) {
@@ -220,6 +238,8 @@ __global__ void __launch_bounds__(kMaxThreads)
   const bool ctx_ok = ctx >= 0 && ctx <= v.l_cap;
   for (int w = tid; w < nbm; w += BD) bitmap[w] = 0;
   for (int w = tid; w < H; w += BD) hash[w] = -1;
+  if (multi)
+    for (int w = tid; w < H; w += BD) first[w] = 0x7fffffff;
   if (tid < 8) misc[tid] = 0;
   lds_barrier();  // Z: LDS cleared (global loads stay in flight)
 
@@ -248,7 +268,28 @@ __global__ void __launch_bounds__(kMaxThreads)
     const int x = r * BD + tid;
     if (x < C) s2p[x] = q2[r];
   }
-  if (debug) {  // repeated positions: LDS open-addressing set of size H
+  int hs[IPT];  // several queries: the entry's hash cell, -1 if none
+  if (multi) {
+    // Open addressing with linear probing; H >= 2 ke > number of distinct
+    // positions, so every probe sequence ends at its key or a free cell.
+#pragma unroll
+    for (int r = 0; r < IPT; ++r) {
+      hs[r] = -1;
+      if (cls[r] != kRes && cls[r] != kMiss) continue;
+      uint32_t h = ((uint32_t)p[r] * 2654435761u) & (uint32_t)(H - 1);
+      while (true) {
+        const int prev = atomicCAS(&hash[h], -1, p[r]);
+        if (prev == -1 || prev == p[r]) break;
+        h = (h + 1) & (uint32_t)(H - 1);
+      }
+      atomicMin(&first[h], r * BD + tid);
+      hs[r] = (int)h;
+    }
+    lds_barrier();  // D: the first entry of every position is known
+#pragma unroll
+    for (int r = 0; r < IPT; ++r)
+      if (hs[r] >= 0 && first[hs[r]] != r * BD + tid) cls[r] = kRepeat;
+  } else if (debug) {  // repeated positions: LDS open-addressing set of size H
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
       if (cls[r] == kNone || p[r] < 0) continue;
@@ -273,7 +314,7 @@ __global__ void __launch_bounds__(kMaxThreads)
       cls[r] = kHit;
       atomicOr(&bitmap[slot[r] >> 5], 1u << (slot[r] & 31));
     }
-    npad += __popcll(__ballot(cls[r] == kPad));
+    npad += __popcll(__ballot(cls[r] == kPad || cls[r] == kRepeat));
     nres += __popcll(__ballot(cls[r] == kRes));
     nhit += __popcll(__ballot(cls[r] == kHit));
     flag[r] = cls[r] == kMiss;
@@ -295,7 +336,7 @@ __global__ void __launch_bounds__(kMaxThreads)
 #pragma unroll
     for (int r = 0; r < IPT; ++r) {
       const int i = r * BD + tid;
-      if (i < k) {
+      if (i < ke) {
         out[i] = -1;
         if (sel_copy) sel_copy[(int64_t)b * k + i] = p[r];
       }
@@ -321,9 +362,12 @@ __global__ void __launch_bounds__(kMaxThreads)
     } else if (cls[r] == kPad) {
       out[i] = -1;
     } else if (cls[r] == kRes) {
-      out[i] = C + (int)fast_mod((uint32_t)p[r], (uint32_t)R, v.r_magic);
+      const int s = C + (int)fast_mod((uint32_t)p[r], (uint32_t)R, v.r_magic);
+      out[i] = s;
+      if (multi) eslot[i] = s;
     } else if (cls[r] == kHit) {
       out[i] = slot[r];
+      if (multi) eslot[i] = slot[r];
     }
     if (sel_copy && cls[r] != kNone) sel_copy[(int64_t)b * k + i] = p[r];
   }
@@ -356,6 +400,7 @@ __global__ void __launch_bounds__(kMaxThreads)
       st.pos2slot[pos] = s;
       s2p[s] = pos;
       out[missi[u]] = s;
+      if (multi) eslot[missi[u]] = s;
       missi[u] = s;  // from here on: the slot the j-th miss is fetched into
       atomicOr(&bitmap[s >> 5], 1u << (s & 31));
     } else {
@@ -390,6 +435,11 @@ __global__ void __launch_bounds__(kMaxThreads)
     st.order[base + off[r] + pre[r]] = x;
     st.last_use[x] = t;
     st.slot2pos[x] = s2p[x];
+  }
+  if (multi) {  // repeats: the slot of the position's first entry
+#pragma unroll
+    for (int r = 0; r < IPT; ++r)
+      if (cls[r] == kRepeat) out[r * BD + tid] = eslot[first[hs[r]]];
   }
 
   if (tid == 0) {
@@ -615,7 +665,7 @@ __global__ void __launch_bounds__(256) probe_host_read_kernel(const u32x4* __res
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-ResolveShape resolve_shape(int k, int C, bool debug_validate) {
+ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries) {
   // Fewest items per thread that fit 1024 threads; then the fewest 64-lane
   // waves that cover max(k, C) with that many items each.
   const int n = k > C ? k : C;
@@ -633,20 +683,25 @@ ResolveShape resolve_shape(int k, int C, bool debug_validate) {
   if (s.items == 0) return s;
   const int W = s.threads / 64;
   size_t words = (size_t)((C + 31) / 32) + C + 2 * (size_t)k + 2 * (size_t)s.items * W + 8;
-  if (debug_validate) words += (size_t)(2 << (31 - __builtin_clz((unsigned)k)));
+  if (multi_entries > 0)
+    words += 2 * (size_t)(2 << (31 - __builtin_clz((unsigned)(2 * multi_entries - 1))));
+  else if (debug_validate)
+    words += (size_t)(2 << (31 - __builtin_clz((unsigned)k)));
   s.lds_bytes = 4 * words;
   return s;
 }
 
 hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const int32_t* sel,
-                          const int32_t* ctx_len, int32_t* out, int32_t* sel_copy) {
-  const ResolveShape sh = resolve_shape(v.k, v.C, (v.flags & HISPARSE_DEBUG_VALIDATE) != 0);
+                          const int32_t* ctx_len, int32_t* out, int32_t* sel_copy,
+                          int multi_entries) {
+  const ResolveShape sh =
+      resolve_shape(v.k, v.C, (v.flags & HISPARSE_DEBUG_VALIDATE) != 0, multi_entries);
   const dim3 grid(v.B), block(sh.threads);
   switch (sh.items) {
 #define HSP_RESOLVE_CASE(N)                                                                     \
   case N:                                                                                       \
     hipLaunchKernelGGL(resolve_kernel<N>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len, \
-                       out, sel_copy);                                                          \
+                       out, sel_copy, multi_entries);                                           \
     break;
     HSP_RESOLVE_CASE(1)
     HSP_RESOLVE_CASE(2)

@@ -112,6 +112,7 @@ struct hisparse {
   std::vector<uint8_t> pending;  // per layer: a prefetch waits to be joined
   std::vector<hipEvent_t> ev_fork, ev_done;
   int fetch_grid_x = 64;  // fetch kernel workgroups
+  size_t lds_max = 0;     // LDS bytes per workgroup of the device
   // timing of eager calls
   bool timing = false;
   std::vector<TimedCall> pool;
@@ -147,7 +148,7 @@ bool capturing(hipStream_t s) {
 
 // resolve kernel (+ fetch unless NO_IO) of one layer on one stream
 int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_t* ctx_len,
-                    int layer, int32_t* out, int32_t* sel_copy) {
+                    int layer, int32_t* out, int32_t* sel_copy, int multi_entries = 0) {
   const bool io = !(h->cfg.flags & HISPARSE_NO_IO);
   TimedCall* tc = nullptr;
   if (h->timing && !capturing(s)) {
@@ -159,7 +160,7 @@ int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_
     tc->fetched = io && !h->view.fuse_fetch;
     HIP_TRY(hipEventRecord(tc->e0, s));
   }
-  HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy));
+  HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy, multi_entries));
   if (tc) HIP_TRY(hipEventRecord(tc->e1, s));
   if (io && !h->view.fuse_fetch) {
     HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
@@ -276,6 +277,7 @@ int hisparse_create(const hisparse_config* cfg, void* const* host_rows, void* de
     if (e != hipSuccess) { release(h); return hip_fail(e, "hipDeviceGetAttribute"); }
     const ResolveShape sh =
         resolve_shape(cfg->top_k, cfg->cache_slots, (cfg->flags & HISPARSE_DEBUG_VALIDATE) != 0);
+    h->lds_max = (size_t)lds_max;
     if (sh.lds_bytes > (size_t)lds_max) {
       release(h);
       return fail(HISPARSE_ERR_UNSUPPORTED, "C=%d, k=%d need %zu bytes of LDS; the device has %d",
@@ -371,6 +373,31 @@ int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel, const
     return HISPARSE_OK;
   }
   return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr);
+}
+
+int hisparse_resolve_multi(hisparse_t h, hipStream_t stream, const int32_t* sel,
+                           int32_t queries, int32_t per_query, const int32_t* ctx_len,
+                           int32_t layer, int32_t* out_slot) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  if (!sel || !ctx_len || !out_slot)
+    return fail(HISPARSE_ERR_INVALID_ARG, "sel, ctx_len and out_slot must not be NULL");
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
+  if (queries < 1 || per_query < 1 || (int64_t)queries * per_query > h->cfg.top_k)
+    return fail(HISPARSE_ERR_INVALID_ARG,
+                "queries (%d) x per_query (%d) must be in [1, top_k = %d]", queries, per_query,
+                h->cfg.top_k);
+  if (h->pending[layer])
+    return fail(HISPARSE_ERR_STATE, "layer %d has a pending prefetch: join it with hisparse_resolve",
+                layer);
+  const int ke = queries * per_query;
+  const ResolveShape sh = resolve_shape(h->cfg.top_k, h->cfg.cache_slots,
+                                        (h->cfg.flags & HISPARSE_DEBUG_VALIDATE) != 0, ke);
+  if (sh.lds_bytes > h->lds_max)
+    return fail(HISPARSE_ERR_UNSUPPORTED,
+                "C=%d with %d entries per request needs %zu bytes of LDS; the device has %zu",
+                h->cfg.cache_slots, ke, sh.lds_bytes, h->lds_max);
+  return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr, ke);
 }
 
 int hisparse_prefetch(hisparse_t h, hipStream_t main_stream, hipStream_t side_stream,

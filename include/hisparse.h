@@ -193,6 +193,29 @@ int hisparse_destroy(hisparse_t h);
 int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel,
                      const int32_t* ctx_len, int32_t layer, int32_t* out_slot);
 
+/* Resolve one layer for several query tokens per request at once (multi-
+ * token prediction or speculative decoding), on `stream`.
+ *   sel:      device int32 [B, queries, per_query]: each query's selections,
+ *             -1 = padding; positions may repeat across and within queries;
+ *   queries x per_query <= top_k;
+ *   out_slot: device int32 [B, queries, per_query]: the slot holding each
+ *             entry's position after the call, -1 for padding.
+ * The queries of a step attend through the same cache, so the step resolves
+ * the union of their selections once (one clock tick per stream): the union
+ * is taken in first-occurrence order over the entries (query-major), every
+ * missing position is fetched once, and every entry is served by its
+ * position's slot.  The per-stream counters are those of the union padded
+ * to queries x per_query entries (repeats count as padding).  A row with an
+ * entry outside [-1, ctx) is rejected as by hisparse_resolve.
+ * [P2 Timeline: multi-token prediction is listed among the features the
+ * method works with; the union reading is this library's.]
+ * Errors: INVALID_ARG (NULL pointer, bad layer, queries x per_query outside
+ * [1, top_k]), STATE (the layer has a pending prefetch), UNSUPPORTED (the
+ * deduplication table does not fit the device's LDS), HIP. */
+int hisparse_resolve_multi(hisparse_t h, hipStream_t stream, const int32_t* sel,
+                           int32_t queries, int32_t per_query, const int32_t* ctx_len,
+                           int32_t layer, int32_t* out_slot);
+
 /* Resolve `layer` early on `side_stream`, ordered after the work already
  * enqueued on `main_stream` (event fork), for models whose layers share one
  * selection.  The next hisparse_resolve of that layer on `main_stream` joins

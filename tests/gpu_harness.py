@@ -99,18 +99,19 @@ class GpuInstance:
 class LockstepRun:
     """A workload run on the GPU next to the oracle (on a subset of streams).
 
-    mode: "eager" (one resolve call per layer) or "graph" (each step's layer
-    calls captured once into a HIP graph and replayed, as the benchmark does).
+    queries > 1: every row holds that many query tokens' selections end to
+    end (k/queries each) and the steps go through hisparse_resolve_multi.
     """
 
     def __init__(self, cfg: Workload, oracle_streams=None, flags: int = 0,
-                 host_flags: int = hb.HISPARSE_HOST_COHERENT, fill_all=False):
+                 host_flags: int = hb.HISPARSE_HOST_COHERENT, fill_all=False, queries: int = 1):
         import torch
         self.torch = torch
         self.cfg = cfg
+        self.queries = queries
         all_streams = [(b, l) for b in range(cfg.B) for l in range(cfg.layers)]
         self.oracle_streams = all_streams if oracle_streams is None else list(oracle_streams)
-        self.trace = make_trace(cfg)
+        self.trace = make_trace(cfg, queries=queries)
         self.gpu = GpuInstance(cfg, flags=flags, host_flags=host_flags)
         if fill_all:
             for (b, l) in all_streams:
@@ -145,11 +146,17 @@ class LockstepRun:
     def gpu_step(self, s: int, layers=None):
         layers = range(self.cfg.layers) if layers is None else layers
         for l in layers:
-            hb.hisparse_resolve(self.gpu.h, self.gpu.stream, self.sel_dev[s, l].data_ptr(),
-                                self.ctx_dev[s].data_ptr(), l, self.out_dev[l].data_ptr())
+            if self.queries > 1:
+                hb.hisparse_resolve_multi(self.gpu.h, self.gpu.stream,
+                                          self.sel_dev[s, l].data_ptr(), self.queries,
+                                          self.cfg.k // self.queries, self.ctx_dev[s].data_ptr(),
+                                          l, self.out_dev[l].data_ptr())
+            else:
+                hb.hisparse_resolve(self.gpu.h, self.gpu.stream, self.sel_dev[s, l].data_ptr(),
+                                    self.ctx_dev[s].data_ptr(), l, self.out_dev[l].data_ptr())
 
     def oracle_step(self, s: int):
-        return self.oracle.step(s, self.trace, no_io=self.no_io)
+        return self.oracle.step(s, self.trace, no_io=self.no_io, queries=self.queries)
 
     def compare_step(self, s: int, res, full_state=True, contents=True, host_rows=True):
         """Element-by-element comparison of one step on every oracle stream."""

@@ -9,10 +9,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle.oracle import OracleStream
+from oracle.oracle import OracleStream, resolve_multi
 from workload import rows as wrows
 from workload.configs import Workload
-from workload.traces import full_trace, touched_positions
+from workload.traces import full_trace, multi_query_trace, touched_positions
 
 
 def small_variant(cfg: Workload, **kw) -> Workload:
@@ -21,7 +21,9 @@ def small_variant(cfg: Workload, **kw) -> Workload:
     return cfg.scaled(**kw)
 
 
-def make_trace(cfg: Workload, streams=None) -> np.ndarray:
+def make_trace(cfg: Workload, streams=None, queries: int = 1) -> np.ndarray:
+    if queries > 1:
+        return multi_query_trace(cfg, queries, streams=streams)
     return full_trace(cfg, streams=streams)
 
 
@@ -60,7 +62,16 @@ class OracleRun:
         for (b, l), st in self.st.items():
             st.append(appended_row(self.cfg, b, l, p), p)
 
-    def step(self, s: int, trace: np.ndarray, no_io: bool = False):
+    def step(self, s: int, trace: np.ndarray, no_io: bool = False, queries: int = 1):
+        """One step on every stream; with queries > 1 each trace row holds the
+        queries' selections end to end and `out` comes back flattened."""
         ctx = self.cfg.ctx_at(s)
+        if queries > 1:
+            res = {}
+            for (b, l), st in self.st.items():
+                r = resolve_multi(st, trace[s, l, b].reshape(queries, -1), ctx, no_io=no_io)
+                r.out = r.out.reshape(-1)
+                res[(b, l)] = r
+            return res
         return {(b, l): st.resolve(trace[s, l, b], ctx, no_io=no_io)
                 for (b, l), st in self.st.items()}

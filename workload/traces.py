@@ -24,6 +24,13 @@ Replacement distributions:
              [0, ctx - R) and otherwise Zipf distance; a rejected draw is
              redrawn from the same branch.
 
+Several query tokens per step (multi-token prediction, speculative
+decoding): query 0 follows the process above with k/Q positions; each other
+query keeps a uniform random subset of ``overlap_pct`` percent of query 0's
+positions (neighbouring tokens attend to much the same history) and draws the
+rest from the replacement distribution, distinct from query 0's row, then is
+put in a seeded random order.  The Q rows are laid end to end.
+
 This module holds none of the method's arithmetic.
 """
 from __future__ import annotations
@@ -147,6 +154,45 @@ def full_trace(cfg: Workload, steps: int | None = None, streams=None) -> np.ndar
             if key not in cache:
                 cache[key] = stream_trace(cfg, b, l, steps)
             out[:, l, b, :] = cache[key]
+    return out
+
+
+def multi_query_trace(cfg: Workload, queries: int, overlap_pct: int = 75,
+                      steps: int | None = None, streams=None) -> np.ndarray:
+    """Selections of ``queries`` query tokens per step: int32 [steps, layers,
+    B, k], each row the Q query rows of k/Q positions laid end to end."""
+    if queries < 1 or cfg.k % queries:
+        raise ValueError("k must be a multiple of the number of queries")
+    steps = cfg.steps if steps is None else steps
+    kq = cfg.k // queries
+    n_keep = overlap_pct * kq // 100
+    base = full_trace(cfg.scaled(k=kq), steps=steps, streams=streams)   # query 0
+    out = np.full((steps, cfg.layers, cfg.B, cfg.k), -1, np.int32)
+    want = None if streams is None else set(streams)
+    done = {}
+    for l in range(cfg.layers):
+        for b in range(cfg.B):
+            if want is not None and (b, l) not in want:
+                continue
+            key = (b, 0) if cfg.shared_selection else (b, l)
+            if key in done:
+                out[:, l, b] = done[key]
+                continue
+            rows = np.empty((steps, cfg.k), np.int32)
+            for st in range(steps):
+                ctx = cfg.ctx_at(st)
+                row0 = base[st, l, b].astype(np.int64)
+                rows[st, :kq] = row0
+                for q in range(1, queries):
+                    rng = np.random.default_rng(
+                        np.random.SeedSequence([cfg.trace_seed, 17, key[0], key[1], st, q]))
+                    taken = np.zeros(ctx, bool)
+                    taken[row0] = True
+                    kept = rng.choice(row0, n_keep, replace=False)
+                    new = _new_positions(cfg, rng, ctx, kq - n_keep, taken)
+                    rows[st, q * kq:(q + 1) * kq] = rng.permutation(np.concatenate([kept, new]))
+            done[key] = rows
+            out[:, l, b] = rows
     return out
 
 
