@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--mla-attention", action="store_true",
                     help="time sparse MLA decode attention over the slot map (one layer)")
     ap.add_argument("--heads", type=int, default=16, help="query heads for --mla-attention")
+    ap.add_argument("--queries", type=int, default=1,
+                    help="query tokens per request and step (multi-token prediction): each "
+                         "brings the workload's k selections; resolved in one pass per layer")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="summarize rocprofv3 CSV output in DIR into profiles/ and exit")
     ap.add_argument("--label", help="summary name (with --summarize-rocprof)")
@@ -77,14 +80,14 @@ def log(msg):
 class Setup:
     """Host histories, two library instances (IO and no-IO) and device inputs."""
 
-    def __init__(self, cfg, host_flags):
+    def __init__(self, cfg, host_flags, queries=1):
         import torch
         from hierarchical_kv_cache_hisparse_amd import binding as hb
         from tests.gpu_harness import GpuInstance, host_view
         from tests.harness import appended_row, fill_host, make_trace
-        self.torch, self.hb, self.cfg = torch, hb, cfg
+        self.torch, self.hb, self.cfg, self.queries = torch, hb, cfg, queries
         t0 = time.time()
-        self.trace = make_trace(cfg)                                   # [S, L, B, k]
+        self.trace = make_trace(cfg, queries=queries)                  # [S, L, B, k]
         nbytes = cfg.l_cap * cfg.row_bytes
         self.hosts = {}
         for l in range(cfg.layers):
@@ -127,8 +130,13 @@ class Setup:
         for l in range(cfg.layers):
             if cfg.growth and s > 0:
                 hb.hisparse_append(inst.h, st, l, self.rows[s, l].data_ptr(), self.pos[s].data_ptr())
-            hb.hisparse_resolve(inst.h, st, self.sel[s, l].data_ptr(), self.ctx[s].data_ptr(), l,
-                                self.out[l].data_ptr())
+            if self.queries > 1:
+                hb.hisparse_resolve_multi(inst.h, st, self.sel[s, l].data_ptr(), self.queries,
+                                          cfg.k // self.queries, self.ctx[s].data_ptr(), l,
+                                          self.out[l].data_ptr())
+            else:
+                hb.hisparse_resolve(inst.h, st, self.sel[s, l].data_ptr(), self.ctx[s].data_ptr(),
+                                    l, self.out[l].data_ptr())
 
     def totals(self, inst):
         """Summed running counters of every stream (misses, evictions, hits)."""
@@ -464,7 +472,7 @@ def cpu_baseline(setup, steps, threads=1):
         for s in range(steps):
             if cfg.growth and s > 0:
                 run.append(s)
-            run.step(s, setup.trace)
+            run.step(s, setup.trace, queries=setup.queries)
 
     elapsed, entries, reps = 0.0, 0, 0
     with ThreadPoolExecutor(threads) as pool:
@@ -497,9 +505,12 @@ def main():
     if args.steps is None:
         args.steps = base.steps
     S = max(args.steps, args.warmup, 1)
+    Q = max(1, args.queries)
     cfg = base.scaled(steps=S) if S != base.steps else base
+    if Q > 1:   # Q query tokens, each with the workload's k selections
+        cfg = cfg.scaled(k=Q * base.k)
     host_flags = hb.HISPARSE_HOST_NONCOHERENT if args.host_noncoherent else hb.HISPARSE_HOST_COHERENT
-    setup = Setup(cfg, host_flags)
+    setup = Setup(cfg, host_flags, queries=Q)
     K, W = args.steps, args.warmup
     io = setup.io
     if args.mla_attention:
@@ -608,6 +619,19 @@ def main():
                            "GBps_over_fetch_kernels": round(fetch_gbps, 3),
                            "GBps_over_timed_region": round(miss_bytes / elapsed / 1e9, 3)},
         }
+
+        if Q > 1:
+            result["metric"] = "resolved query-token entries/s, several query tokens per step"
+            result["config"]["queries"] = Q
+            result["config"]["selections_per_query"] = cfg.k // Q
+            result["config"]["top_k"] = cfg.k
+            distinct = tot_hit + tot_miss
+            result["multi_query"] = {
+                "entries_per_request_step": cfg.k,
+                "avg_distinct_nonresident_per_request_step": round(
+                    distinct / max(1, K * cfg.layers * cfg.B), 1),
+                "reading": "the union of the queries' selections is resolved once per layer "
+                           "call; every entry is served its position's slot"}
 
         if not args.only_timed:
             # ---- graph replay (IO and no-IO) -------------------------------
