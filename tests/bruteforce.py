@@ -104,3 +104,21 @@ class BruteStream:
 
     def slot2pos(self):
         return [-1 if p is None else p for p in self.held]
+
+
+def brute_topk(scores, ctx: int, k: int):
+    """Top-k by exhaustive search over position subsets (tiny ctx only), as a
+    different formulation from the oracle's sort: the chosen set has the
+    largest score vector (sorted descending, compared lexicographically),
+    and among sets with that vector the smallest sorted position list.
+    Returns ascending positions padded with -1 to k."""
+    import itertools
+    m = min(k, ctx)
+    best = None
+    for subset in itertools.combinations(range(ctx), m):
+        key = (tuple(sorted((float(scores[i]) for i in subset), reverse=True)),
+               tuple(-i for i in subset))
+        if best is None or key > best[0]:
+            best = (key, subset)
+    chosen = list(best[1]) if best else []
+    return chosen + [-1] * (k - len(chosen))
