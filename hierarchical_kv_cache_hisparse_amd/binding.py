@@ -112,6 +112,8 @@ def library():
             "hisparse_probe_host_read": [P, P, P, SZ, I32],
             "hisparse_mla_workspace_bytes": [P, I32, P],
             "hisparse_sparse_mla_decode": [P, P, I32, P, P, I32, ctypes.c_float, P, P, P],
+            "hisparse_topk_workspace_bytes": [I32, ctypes.c_int64, P],
+            "hisparse_topk": [P, P, ctypes.c_int64, I32, ctypes.c_int64, P, I32, P, P],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -249,3 +251,16 @@ def hisparse_sparse_mla_decode(h, stream: int, layer: int, q: int, out_slot: int
     _check(library().hisparse_sparse_mla_decode(h, stream, layer, q, out_slot, num_heads,
                                                 scale, workspace, out, lse),
            "hisparse_sparse_mla_decode")
+
+
+def hisparse_topk_workspace_bytes(num_rows: int, max_len: int) -> int:
+    n = ctypes.c_size_t()
+    _check(library().hisparse_topk_workspace_bytes(num_rows, max_len, ctypes.byref(n)),
+           "hisparse_topk_workspace_bytes")
+    return n.value
+
+
+def hisparse_topk(stream: int, scores: int, row_stride: int, num_rows: int, max_len: int,
+                  ctx_len: int, k: int, workspace: int, out_sel: int) -> None:
+    _check(library().hisparse_topk(stream, scores, row_stride, num_rows, max_len, ctx_len, k,
+                                   workspace, out_sel), "hisparse_topk")

@@ -104,6 +104,38 @@ hipError_t launch_append(const StreamView& v, hipStream_t s, int layer, const ui
 hipError_t launch_probe_host_read(hipStream_t s, const void* host, void* dev, size_t bytes,
                                   int workgroups);
 
+// ---- top-k selection over indexer scores ---------------------------------------
+constexpr int kTopkChunk = 4096;          // positions per workgroup of the scan kernels
+constexpr int kTopkThreads = 256;         // threads of the scan kernels
+constexpr int kTopkBins = 4096;           // level-1 histogram: top 12 key bits
+constexpr int kTopkFinishThreads = 1024;  // one workgroup per row
+constexpr int kTopkCntStride = 64;        // candidate counter words per row
+constexpr int kTopkMaxRows = 65535;       // grid.y of the scan kernels
+constexpr int64_t kTopkMaxLen = (int64_t(1) << 31) - kTopkChunk;
+
+struct TopkArgs {
+  const float* scores;    // [rows][row_stride]
+  int64_t row_stride;     // floats between rows (multiple of 4)
+  int64_t max_len;        // positions per row the workspace is sized for
+  const int32_t* ctx_len; // [rows]: eligible positions [0, ctx), clamped
+  int32_t k;
+  int32_t rows;
+  uint32_t* hist;         // [rows][4096], zero between calls
+  uint32_t* cnt;          // [rows][64], word 0 = candidates, zero between calls
+  uint32_t* bitmap;       // [rows][bm_words]
+  int64_t bm_words;
+  uint32_t* cand;         // [rows][max_len][2]: (key, position)
+  int32_t* out;           // [rows][k]
+};
+
+struct TopkLayout {
+  size_t hist, cnt, bitmap, cand, total;  // byte offsets in the workspace
+  int64_t bm_words;
+};
+
+TopkLayout topk_layout(int rows, int64_t max_len);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
 // ---- sparse MLA decode attention over the slot map ----------------------------
 constexpr int kMlaDqk = 576;        // latent 512 + rope 64 (bf16)
 constexpr int kMlaDv = 512;         // value = the latent part

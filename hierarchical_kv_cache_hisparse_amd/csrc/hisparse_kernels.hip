@@ -31,6 +31,7 @@
 //     the slot rows in HBM.  No MFMA anywhere: nothing here is a contraction.
 #include <hip/hip_runtime.h>
 
+#include "hisparse_device.h"
 #include "hisparse_internal.h"
 
 namespace hsp {
@@ -65,30 +66,6 @@ __device__ __forceinline__ StreamPtrs stream_ptrs(const StreamView& v, int layer
 
 __device__ __forceinline__ uint32_t* status_word(const StreamView& v) {
   return (uint32_t*)v.meta;
-}
-
-// Workgroup barrier for LDS only.  No wave of the resolve kernel reads global
-// memory that another wave of it wrote, so a barrier never has to wait for
-// outstanding global stores (HIP's __syncthreads would: it fences global
-// memory too, which costs a store round trip per barrier).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
-// 1, 2, 4, 8 inside each 16-lane row, then the row totals are carried with
-// the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2
-// and 3).  Six VALU operations, no LDS traffic.
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
 }
 
 // Quotient and remainder of p < 2^31 by d >= 1, given magic = floor(2^32/d)

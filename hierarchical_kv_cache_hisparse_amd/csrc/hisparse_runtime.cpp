@@ -578,6 +578,56 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
   return HISPARSE_OK;
 }
 
+namespace {
+int check_topk(int32_t num_rows, int64_t max_len) {
+  if (num_rows < 1 || num_rows > kTopkMaxRows)
+    return fail(HISPARSE_ERR_INVALID_ARG, "num_rows %d outside [1, %d]", num_rows, kTopkMaxRows);
+  if (max_len < 1 || max_len > kTopkMaxLen)
+    return fail(HISPARSE_ERR_INVALID_ARG, "max_len %lld outside [1, %lld]", (long long)max_len,
+                (long long)kTopkMaxLen);
+  return HISPARSE_OK;
+}
+}  // namespace
+
+int hisparse_topk_workspace_bytes(int32_t num_rows, int64_t max_len, size_t* bytes) {
+  int rc = check_topk(num_rows, max_len);
+  if (rc) return rc;
+  if (!bytes) return fail(HISPARSE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = topk_layout(num_rows, max_len).total;
+  return HISPARSE_OK;
+}
+
+int hisparse_topk(hipStream_t stream, const float* scores, int64_t row_stride, int32_t num_rows,
+                  int64_t max_len, const int32_t* ctx_len, int32_t k, void* workspace,
+                  int32_t* out_sel) {
+  int rc = check_topk(num_rows, max_len);
+  if (rc) return rc;
+  if (!scores || !ctx_len || !workspace || !out_sel)
+    return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  if (k < 1 || k > kMaxTopK) return fail(HISPARSE_ERR_INVALID_ARG, "k %d outside [1, %d]", k, kMaxTopK);
+  if (row_stride < max_len || row_stride % 4)
+    return fail(HISPARSE_ERR_INVALID_ARG, "row_stride must be >= max_len and a multiple of 4");
+  if (reinterpret_cast<uintptr_t>(scores) % 16 || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(HISPARSE_ERR_INVALID_ARG, "scores must be 16-byte and workspace 256-byte aligned");
+  const TopkLayout lay = topk_layout(num_rows, max_len);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  TopkArgs a{};
+  a.scores = scores;
+  a.row_stride = row_stride;
+  a.max_len = max_len;
+  a.ctx_len = ctx_len;
+  a.k = k;
+  a.rows = num_rows;
+  a.hist = reinterpret_cast<uint32_t*>(w + lay.hist);
+  a.cnt = reinterpret_cast<uint32_t*>(w + lay.cnt);
+  a.bitmap = reinterpret_cast<uint32_t*>(w + lay.bitmap);
+  a.bm_words = lay.bm_words;
+  a.cand = reinterpret_cast<uint32_t*>(w + lay.cand);
+  a.out = out_sel;
+  HIP_TRY(launch_topk(a, stream));
+  return HISPARSE_OK;
+}
+
 const char* hisparse_strerror(int code) {
   switch (code) {
     case HISPARSE_OK: return "success";

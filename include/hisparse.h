@@ -304,6 +304,39 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
                                const int32_t* out_slot, int32_t num_heads, float scale,
                                void* workspace, float* out, float* lse);
 
+/* ---- top-k selection over indexer scores ----------------------------------
+ * The step before resolution: from one score per position (a token for
+ * DSA-style per-layer selection, a 16-token page for Quest-style selection),
+ * pick the positions the resolver is handed.  [P3 Abstract: decoding attends
+ * to the top-k positions an indexer selects, and the hierarchical cache does
+ * not depend on which indexer; P2 Timeline: token- and page-granular
+ * selection.]  Readings (the pages give none): among positions [0, ctx) the
+ * k largest scores are taken, equal scores going to the lower position, -0
+ * equal to +0; the row is written in ascending position order (the pages
+ * give a selection no order) and padded with -1 when ctx < k.  Scores must
+ * not be NaN (a NaN is ordered above +inf).
+ *
+ * hisparse_topk_workspace_bytes: device workspace for rows of up to max_len
+ *   positions: a 16 KiB histogram and a counter per row, a position bitmap
+ *   and room for max_len boundary candidates (8 bytes each) per row.  Host
+ *   only.  The workspace must be zero-filled once before its first use;
+ *   every call leaves the parts it needs zeroed again.
+ * hisparse_topk (async on `stream`, graph-capturable: three launches, no
+ *   memset; calls sharing a workspace must be ordered):
+ *   scores:     device fp32, row b at scores + b * row_stride, 16-byte
+ *               aligned, row_stride >= max_len and a multiple of 4;
+ *   num_rows:   1..65535 (e.g. requests of one layer);
+ *   max_len:    1..2^31 - 4097, the workspace's row capacity;
+ *   ctx_len:    device int32 [num_rows]; clamped to [0, max_len];
+ *   k:          1..4096;
+ *   out_sel:    device int32 [num_rows, k]: ready to pass to
+ *               hisparse_resolve as `sel` (with the same ctx_len).
+ * Errors: INVALID_ARG (NULL, misaligned, sizes out of range), HIP. */
+int hisparse_topk_workspace_bytes(int32_t num_rows, int64_t max_len, size_t* bytes);
+int hisparse_topk(hipStream_t stream, const float* scores, int64_t row_stride, int32_t num_rows,
+                  int64_t max_len, const int32_t* ctx_len, int32_t k, void* workspace,
+                  int32_t* out_sel);
+
 /* Text for a return code, and the last failure of the calling thread. */
 const char* hisparse_strerror(int code);
 const char* hisparse_last_error(void);
