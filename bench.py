@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--mla-attention", action="store_true",
                     help="time sparse MLA decode attention over the slot map (one layer)")
     ap.add_argument("--heads", type=int, default=16, help="query heads for --mla-attention")
+    ap.add_argument("--topk", action="store_true",
+                    help="time the top-k selection producer over synthetic indexer scores at "
+                         "the workload's per-layer shape (requests x context rows, k)")
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per request and step (multi-token prediction): each "
                          "brings the workload's k selections; resolved in one pass per layer")
@@ -455,6 +458,96 @@ def mla_study(setup, K, H):
                                        f"last step, scaled to all requests"}}
 
 
+def topk_study(cfg, K, W):
+    """hisparse_topk on one layer's scores (requests x context rows, the
+    workload's k), on fresh drifting scores each step; torch events on the
+    launching stream around the three launches.
+
+    Algorithmic bytes per call: every eligible score read once (4 B) plus the
+    selection written (4 B per entry).  The kernels read the scores twice
+    (histogram, filter), so at best half the HBM peak is reachable."""
+    import torch
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    from oracle.topk import topk_rows
+    from workload.scores import score_rows
+    B, N, k = cfg.B, cfg.L0, cfg.k
+    stride = ((N + 3) // 4) * 4
+    ws = torch.zeros(hb.hisparse_topk_workspace_bytes(B, N), dtype=torch.uint8, device="cuda:0")
+    n_sets = 4
+    host_scores = [score_rows(B, N, 5000 + cfg.data_seed, 0, s, ties=True) for s in range(n_sets)]
+    scores = torch.zeros((n_sets, B, stride), dtype=torch.float32, device="cuda:0")
+    for i, sc in enumerate(host_scores):
+        scores[i, :, :N].copy_(torch.from_numpy(sc))
+    ctx = torch.full((B,), N, dtype=torch.int32, device="cuda:0")
+    out = torch.empty((B, k), dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call(i):
+        hb.hisparse_topk(stream, scores[i % n_sets].data_ptr(), stride, B, N, ctx.data_ptr(), k,
+                         ws.data_ptr(), out.data_ptr())
+
+    for i in range(W):
+        call(i)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(K):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(times))
+    # the graph-replayed per-call time (launch gaps removed)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            s2 = torch.cuda.current_stream().cuda_stream
+            for i in range(16):
+                hb.hisparse_topk(s2, scores[i % n_sets].data_ptr(), stride, B, N, ctx.data_ptr(),
+                                 k, ws.data_ptr(), out.data_ptr())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) / (5 * 16) * 1e6
+    # parity spot check of the last eager result
+    want = topk_rows(host_scores[(K - 1) % n_sets], [N] * B, k)
+    got = None
+    call(K - 1)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got, want), "top-k result differs from the oracle"
+    # the oracle on the host: as many rows as fit ~10 s (at least one)
+    t_cpu, n_cpu = 0.0, 0
+    for b in range(B):
+        t0 = time.perf_counter()
+        topk_rows(host_scores[0][b:b + 1], [N], k)
+        t_cpu += time.perf_counter() - t0
+        n_cpu += 1
+        if t_cpu > 10.0:
+            break
+    byts = B * N * 4 + B * k * 4
+    return {"metric": "top-k selection over indexer scores", "value": round(us, 3),
+            "unit": "us per layer call", "higher_is_better": False, "workload": cfg.name,
+            "rows": B, "positions_per_row": N, "k": k,
+            "scores_per_s": round(B * N / us * 1e6, 1),
+            "graph_us_per_call": round(graph_us, 3),
+            "roofline": {"bound": "hbm", "achieved": round(byts / us / 1e3, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(byts / us / 1e3 / HBM_PEAK_GBPS, 4),
+                         "per_launch_bytes": byts,
+                         "achieved_graph": round(byts / graph_us / 1e3, 1)},
+            "timing": "torch events around the three launches, median of K calls",
+            "cpu_baseline": {"value": round(t_cpu / n_cpu * B * 1e6, 1), "unit": "us per layer call",
+                             "cores": 1, "kind": "oracle",
+                             "sample": f"numpy lexsort oracle on {n_cpu} of {B} rows, scaled"}}
+
+
 def cpu_baseline(setup, steps, threads=1):
     """The CPU oracle (plain C) on the same trace and host rows, repeated from
     a cold state until at least 3 s of wall time are measured.  With
@@ -504,6 +597,9 @@ def main():
     base = CONFIGS[args.config]
     if args.steps is None:
         args.steps = base.steps
+    if args.topk:
+        print(json.dumps(topk_study(base, max(1, args.steps), args.warmup)), flush=True)
+        return
     S = max(args.steps, args.warmup, 1)
     Q = max(1, args.queries)
     cfg = base.scaled(steps=S) if S != base.steps else base

@@ -108,7 +108,6 @@ hipError_t launch_probe_host_read(hipStream_t s, const void* host, void* dev, si
 constexpr int kTopkChunk = 4096;          // positions per workgroup of the scan kernels
 constexpr int kTopkThreads = 256;         // threads of the scan kernels
 constexpr int kTopkBins = 4096;           // level-1 histogram: top 12 key bits
-constexpr int kTopkFinishThreads = 1024;  // one workgroup per row
 constexpr int kTopkCntStride = 64;        // candidate counter words per row
 constexpr int kTopkMaxRows = 65535;       // grid.y of the scan kernels
 constexpr int64_t kTopkMaxLen = (int64_t(1) << 31) - kTopkChunk;
@@ -120,8 +119,9 @@ struct TopkArgs {
   const int32_t* ctx_len; // [rows]: eligible positions [0, ctx), clamped
   int32_t k;
   int32_t rows;
-  uint32_t* hist;         // [rows][4096], zero between calls
-  uint32_t* cnt;          // [rows][64], word 0 = candidates, zero between calls
+  uint32_t* hist;         // [rows][4096] top-12-bit counts, zero between calls
+  uint32_t* hist2;        // [rows][4096] next-12-bit counts of the candidates, zero between calls
+  uint32_t* cnt;          // [rows][64] counters and the threshold, zero between calls
   uint32_t* bitmap;       // [rows][bm_words]
   int64_t bm_words;
   uint32_t* cand;         // [rows][max_len][2]: (key, position)
@@ -129,7 +129,7 @@ struct TopkArgs {
 };
 
 struct TopkLayout {
-  size_t hist, cnt, bitmap, cand, total;  // byte offsets in the workspace
+  size_t hist, hist2, cnt, bitmap, cand, total;  // byte offsets in the workspace
   int64_t bm_words;
 };
 

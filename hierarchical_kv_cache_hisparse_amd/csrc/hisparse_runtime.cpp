@@ -619,6 +619,7 @@ int hisparse_topk(hipStream_t stream, const float* scores, int64_t row_stride, i
   a.k = k;
   a.rows = num_rows;
   a.hist = reinterpret_cast<uint32_t*>(w + lay.hist);
+  a.hist2 = reinterpret_cast<uint32_t*>(w + lay.hist2);
   a.cnt = reinterpret_cast<uint32_t*>(w + lay.cnt);
   a.bitmap = reinterpret_cast<uint32_t*>(w + lay.bitmap);
   a.bm_words = lay.bm_words;

@@ -321,7 +321,7 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
  *   and room for max_len boundary candidates (8 bytes each) per row.  Host
  *   only.  The workspace must be zero-filled once before its first use;
  *   every call leaves the parts it needs zeroed again.
- * hisparse_topk (async on `stream`, graph-capturable: three launches, no
+ * hisparse_topk (async on `stream`, graph-capturable: two launches, no
  *   memset; calls sharing a workspace must be ordered):
  *   scores:     device fp32, row b at scores + b * row_stride, 16-byte
  *               aligned, row_stride >= max_len and a multiple of 4;
