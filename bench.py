@@ -199,19 +199,25 @@ def link_probe(torch, hb):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "hierarchical_kv_cache_hisparse_amd", "csrc",
-                             "hisparse_kernels.hip")
+# the resolve and fetch kernels' sources: PMC summaries taken on other sources
+# are not used for the traffic figure
+KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_kv_cache_hisparse_amd", "csrc", f)
+                  for f in ("hisparse_kernels.hip", "hisparse_device.h", "hisparse_internal.h")]
 CALIBRATION_BYTES = 256 << 20
 
 
 def kernel_source_sha():
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def short_kernel_name(name):
-    for key in ("mla_decode_kernel", "mla_combine_kernel", "resolve_kernel", "fetch_kernel",
+    for key in ("mla_decode_kernel", "mla_combine_kernel", "topk_hist_kernel", "topk_filter_kernel",
+                "topk_finish_kernel", "resolve_kernel", "fetch_kernel",
                 "probe_host_read_kernel", "init_kernel",
                 "load_window_kernel", "append_kernel", "prefetch_join_kernel"):
         if key in name:
@@ -548,9 +554,9 @@ def topk_study(cfg, K, W):
                              "sample": f"numpy lexsort oracle on {n_cpu} of {B} rows, scaled"}}
 
 
-def cpu_baseline(setup, steps, threads=1):
+def cpu_baseline(setup, steps, threads=1, min_seconds=10.0):
     """The CPU oracle (plain C) on the same trace and host rows, repeated from
-    a cold state until at least 3 s of wall time are measured.  With
+    a cold state until at least `min_seconds` of wall time are measured.  With
     threads > 1 the independent streams are spread over that many threads
     (the C oracle runs without the Python lock)."""
     from concurrent.futures import ThreadPoolExecutor
@@ -569,7 +575,7 @@ def cpu_baseline(setup, steps, threads=1):
 
     elapsed, entries, reps = 0.0, 0, 0
     with ThreadPoolExecutor(threads) as pool:
-        while elapsed < 3.0 and reps < 50:
+        while elapsed < min_seconds and reps < 2000:
             t0 = time.perf_counter()
             list(pool.map(run_group, groups))
             elapsed += time.perf_counter() - t0
@@ -789,7 +795,8 @@ def main():
             if not args.no_cpu_baseline:
                 result["cpu_baseline"] = cpu_baseline(setup, K)
                 result["cpu_baseline_threads"] = cpu_baseline(
-                    setup, K, threads=min(cfg.streams, len(os.sched_getaffinity(0))))
+                    setup, K, threads=min(cfg.streams, len(os.sched_getaffinity(0))),
+                    min_seconds=5.0)
     finally:
         setup.close()
     print(json.dumps(result), flush=True)
