@@ -356,6 +356,29 @@ __global__ void __launch_bounds__(kMaxThreads)
   ballot_counts<IPT>(flag, cntB, W, wave, lane, pre);
   lds_barrier();  // 2: misses staged, unreferenced-slot counts
 
+  // ---- fused fetch, first chunks: the missing positions are known, their --
+  // slots are not yet.  Start the first kPre 16-byte host reads per thread
+  // now, so the host link is busy while the victims are chosen and the LRU
+  // order is rebuilt; they are stored once the slots are known.
+  constexpr int kPre = IPT <= 8 ? 4 : 0;
+  const bool fuse = v.fuse_fetch && !(v.flags & HISPARSE_NO_IO);
+  const uint32_t cpr = (uint32_t)(v.row_bytes >> 4);
+  const uint32_t total = fuse ? (uint32_t)M * cpr : 0u;
+  const uint8_t* host = v.host[layer * v.B + b];
+  u32x4 pre_val[kPre > 0 ? kPre : 1];
+  uint32_t pre_c[kPre > 0 ? kPre : 1];
+  int pre_j[kPre > 0 ? kPre : 1];
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const uint32_t g = tid + u * BD;
+    pre_j[u] = -1;
+    if (g < total) {
+      pre_j[u] = (int)fast_div(g, cpr, v.cpr_magic, &pre_c[u]);
+      pre_val[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(host + (int64_t)missp[pre_j[u]] * v.row_bytes) + pre_c[u]);
+    }
+  }
+
   // ---- victims = first M unreferenced slots in LRU order; the j-th miss ----
   // takes the j-th victim.  The victim's owner thread applies the whole miss.
   scan_offsets<IPT>([&](int e) { return cntB[e]; }, W, wave, lane, off);
@@ -437,13 +460,15 @@ __global__ void __launch_bounds__(kMaxThreads)
   // ---- fused miss fetch: the workgroup copies its own missing rows ---------
   // (enough in flight to saturate the host link once a layer call has >= 8
   // streams; with fewer, the separate fan-out fetch kernel is used instead)
-  if (v.fuse_fetch && !(v.flags & HISPARSE_NO_IO)) {
+  if (fuse) {
     constexpr int U = 4;
-    const uint32_t cpr = (uint32_t)(v.row_bytes >> 4);
-    const uint32_t total = (uint32_t)M * cpr;
-    const uint8_t* host = v.host[layer * v.B + b];
     uint8_t* dst = v.cache + (int64_t)(layer * v.B + b) * (C + R) * v.row_bytes;
-    for (uint32_t g0 = tid; g0 < total; g0 += BD * U) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+      if (pre_j[u] >= 0)
+        reinterpret_cast<u32x4*>(dst + (int64_t)missi[pre_j[u]] * v.row_bytes)[pre_c[u]] =
+            pre_val[u];
+    for (uint32_t g0 = tid + kPre * BD; g0 < total; g0 += BD * U) {
       u32x4 val[U];
       int sl[U];
       uint32_t c[U];
