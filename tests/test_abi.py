@@ -114,3 +114,40 @@ def test_host_alloc_rejects_bad_arguments():
         hb.hisparse_host_alloc(0)
     with pytest.raises(hb.HisparseError):
         hb.hisparse_host_alloc(4096, 0x80)
+
+
+def test_topk_workspace_sizes():
+    """Per row: two 4096-bin histograms, a counter block, one bitmap word per
+    32 positions rounded up to whole 4096-position chunks, and 8 bytes per
+    position for boundary candidates; each part 256-byte aligned."""
+    def align(x):
+        return (x + 255) // 256 * 256
+    for rows, n in ((1, 1), (16, 131072), (16, 262144), (4, 65536), (3, 10001)):
+        words = -(-n // 4096) * 128
+        want = (2 * align(rows * 4096 * 4) + align(rows * 64 * 4) + align(rows * words * 4)
+                + align(rows * n * 8))
+        assert hb.hisparse_topk_workspace_bytes(rows, n) == want, (rows, n)
+
+
+@pytest.mark.parametrize("rows,n", [(0, 100), (65536, 100), (1, 0), (1, (1 << 31) - 4096 + 1)])
+def test_topk_rejects_bad_sizes_on_the_host(rows, n):
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_topk_workspace_bytes(rows, n)
+    assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+    with pytest.raises(hb.HisparseError):
+        hb.hisparse_topk(0, 0, 4, rows, n, 0, 8, 0, 0)
+
+
+def test_topk_rejects_null_and_bad_k_before_any_launch():
+    for k in (0, 4097):
+        with pytest.raises(hb.HisparseError) as e:
+            hb.hisparse_topk(0, 256, 1024, 2, 1024, 256, k, 256, 256)
+        assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+    with pytest.raises(hb.HisparseError):
+        hb.hisparse_topk(0, 0, 1024, 2, 1024, 256, 8, 256, 256)
+
+
+def test_multi_resolve_rejects_a_null_handle():
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_resolve_multi(None, 0, 256, 2, 8, 256, 0, 256)
+    assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
