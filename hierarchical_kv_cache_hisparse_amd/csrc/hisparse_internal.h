@@ -140,7 +140,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 constexpr int kMlaDqk = 576;        // latent 512 + rope 64 (bf16)
 constexpr int kMlaDv = 512;         // value = the latent part
 constexpr int kMlaHB = 16;          // heads per workgroup
-constexpr int kMlaWaves = 8;
+constexpr int kMlaWaves = 4;
 constexpr int kMlaThreads = 64 * kMlaWaves;
 constexpr int kMlaMaxSplits = 256;
 
@@ -169,6 +169,6 @@ struct MlaShape {
 };
 
 MlaShape mla_shape(int B, int H, int k, int T);
-hipError_t launch_mla(const MlaArgs& a, hipStream_t s, size_t lds_bytes, int grid);
+hipError_t launch_mla(const MlaArgs& a, hipStream_t s, size_t lds_bytes);
 
 }  // namespace hsp

@@ -19,25 +19,29 @@
 //
 // CDNA4 mapping:
 //   * grid = (requests x head blocks of 16) x splits of the token rows, about
-//     one workgroup per CU; each workgroup (8 waves, 16 rows each, all row
-//     loads in flight at once) streams its split's rows once from HBM;
-//   * per wave, 16 rows at a time: S^T (16 rows x 16 heads) = K . Q^T with
-//     v_mfma_f32_16x16x32_bf16, the row fragments loaded straight from the
-//     slot rows (16-byte loads), the 16 query heads read from LDS;
-//   * online softmax in fp32 per head; P^T (rows x heads) is already in the
-//     B-operand layout of v_mfma_f32_16x16x16_bf16, so O^T += V^T . P^T needs
-//     only V transposed: the wave's rows go through a private LDS buffer;
-//     P is split into bf16 hi + lo parts (two MFMAs) so the products keep
-//     ~16 more bits than a plain bf16 P;
-//   * the 8 waves combine through a fixed-order tree in LDS (bit-reproducible,
-//     reusing the V-tile space); wave 0 writes the split's partial; each split
-//     writes its partial (max, sum, unnormalised output) to a workspace, and a
-//     second kernel (8 workgroups per request and head block, coalesced over
-//     the partials' register order) merges the splits.
+//     two workgroups per CU (71 KiB of LDS each, so one computes while the
+//     other waits for its rows); a workgroup (4 waves) walks its split in
+//     tiles of 64 rows, each row read once from HBM (16-byte loads, all in
+//     flight, the next tile's requested while the current one is finished);
+//   * scores: wave w takes rows 16w .. 16w+15 of the tile, S^T (16 rows x 16
+//     heads) = K . Q^T with v_mfma_f32_16x16x32_bf16, row fragments straight
+//     from the slot rows, the 16 query heads' fragments held in registers;
+//   * online softmax in fp32 with one running max per head for the whole
+//     workgroup (the waves exchange their tile maxima through LDS), so every
+//     wave scales its rows the same way;
+//   * values: the tile's V part (512 dims) and P^T (hi and lo bf16 parts,
+//     so the products keep ~16 more bits than a plain bf16 P) go to LDS, and
+//     wave w accumulates O^T for output dims 128w .. 128w+127 over the 64 rows
+//     with v_mfma_f32_16x16x16_bf16: the waves own disjoint dims, so nothing
+//     is combined across waves but the softmax sums;
+//   * each split writes its partial (max, sum, unnormalised output) to a
+//     workspace, and a second kernel (8 workgroups per request and head
+//     block, coalesced over the partials' register order) merges the splits.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 
+#include "hisparse_device.h"
 #include "hisparse_internal.h"
 
 namespace hsp {
@@ -48,13 +52,16 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKSteps = kMlaDqk / 32;  // 18 steps of 32 dims for the scores
+constexpr int kTile = 16 * kMlaWaves;   // 64 rows per tile
 constexpr int kVRowPitch = kMlaDv + 8;  // bf16 per LDS row (padding against bank conflicts)
-constexpr size_t kMlaVbufBytes = sizeof(uint16_t) * kMlaWaves * 16 * kVRowPitch;  // 133 KiB
-constexpr size_t kMlaQBytes = sizeof(uint16_t) * kMlaHB * kMlaDqk;               // 18 KiB
-static_assert(kMlaVbufBytes >= sizeof(float) * (kMlaWaves / 2) * kMlaHB * kMlaDv,
-              "the tree-combine buffers alias the V tiles");
-constexpr int kDBlocks = kMlaDv / 16;  // 32 blocks of 16 output dims
-constexpr int kMlaMergeParts = 8;      // merge workgroups per (request, head block)
+constexpr size_t kMlaVbufBytes = sizeof(uint16_t) * kTile * kVRowPitch;     // 65 KiB
+constexpr size_t kMlaPBytes = 2 * sizeof(uint16_t) * kMlaHB * kTile;        // 4 KiB (hi, lo)
+constexpr size_t kMlaRedBytes = sizeof(float) * 2 * kMlaWaves * kMlaHB;     // 0.5 KiB
+constexpr int kDBlocks = kMlaDv / 16;                 // 32 blocks of 16 output dims
+constexpr int kWaveDB = kDBlocks / kMlaWaves;         // 8 blocks (128 dims) per wave
+constexpr int kWgPerCu = 2;                           // workgroups resident per CU
+constexpr int kMlaMergeParts = 8;                     // merge workgroups per (request, head block)
+constexpr int kXcds = 8;                              // MI355X: 8 XCDs, 32 CUs each
 
 __device__ __forceinline__ short bf16_bits(__bf16 x) {
   return __builtin_bit_cast(short, x);
@@ -62,90 +69,106 @@ __device__ __forceinline__ short bf16_bits(__bf16 x) {
 
 __global__ void __launch_bounds__(kMlaThreads) mla_decode_kernel(MlaArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  // [kMlaWaves][16 rows][kVRowPitch] bf16 V tiles; after the row loop the same
-  // space holds the tree-combine buffers ([4][16 heads][512] fp32)
-  __bf16* vbuf = reinterpret_cast<__bf16*>(smem);
-  float* tree = reinterpret_cast<float*>(smem);
-  __bf16* qs = reinterpret_cast<__bf16*>(smem + kMlaVbufBytes);      // [16 heads][576]
-  float* wml = reinterpret_cast<float*>(smem + kMlaVbufBytes + kMlaQBytes);  // [waves][16][2]
+  __bf16* vt = reinterpret_cast<__bf16*>(smem);                       // [64][pitch]
+  short* phi_t = reinterpret_cast<short*>(smem + kMlaVbufBytes);       // [16 heads][64]
+  short* plo_t = phi_t + kMlaHB * kTile;
+  float* red = reinterpret_cast<float*>(smem + kMlaVbufBytes + kMlaPBytes);
+  float* red_m = red;                      // [waves][16] tile maxima
+  float* red_l = red + kMlaWaves * kMlaHB;  // [waves][16] softmax sums
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = lane & 15;  // head (B-operand column, D column)
+  const int h = lane & 15;  // head (B-operand and D column)
   const int g = lane >> 4;  // lane group: k sub-range of the operands, D rows 4g..4g+3
 
+  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs
+  // (XCD = id mod 8), so the head blocks of one (request, split) -- which
+  // read the same rows -- get ids 8 apart: one XCD, dispatched together,
+  // sharing its L2.
   const int id = blockIdx.x;
-  const int split = id % a.S;
-  const int rest = id / a.S;
-  const int hb = rest % a.HBn;
-  const int b = rest / a.HBn;
+  const int xc = id % kXcds;
+  const int qd = id / kXcds;
+  const int hb = qd % a.HBn;
+  const int unit = (qd / a.HBn) * kXcds + xc;  // b * S + split
+  if (unit >= a.B * a.S) return;
+  const int split = unit % a.S;
+  const int b = unit / a.S;
 
-  // this wave's 16 rows: slot lookups first (they gate the row loads)
   const int n_tok = a.k * a.T;
   const int r_begin = split * a.rows_per_split;
   const int r_end = min(n_tok, r_begin + a.rows_per_split);
   const int32_t* slots = a.slots + (int64_t)b * a.k;
   const uint8_t* cbase = a.cache + (int64_t)b * a.stream_bytes;
-
-  // the block's 16 query heads into LDS (16-byte chunks)
-  {
-    const __bf16* qblk = a.q + ((int64_t)b * a.H + hb * kMlaHB) * kMlaDqk;
-    for (int c = tid; c < kMlaHB * kMlaDqk / 8; c += kMlaThreads)
-      reinterpret_cast<bf16x8*>(qs)[c] = reinterpret_cast<const bf16x8*>(qblk)[c];
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  float4_t acc[kDBlocks];
-#pragma unroll
-  for (int db = 0; db < kDBlocks; ++db) acc[db] = float4_t{0.f, 0.f, 0.f, 0.f};
-  __bf16* vb = vbuf + wave * 16 * kVRowPitch;
   const bf16x8 zero8 = {};
-  __syncthreads();  // queries in LDS
 
-  for (int r0 = r_begin + 16 * wave; r0 < r_end; r0 += 16 * kMlaWaves) {
-    // this lane's row (A-operand row m = lane & 15)
-    const int r = r0 + (lane & 15);
-    bool valid = false;
-    const uint8_t* rowp = cbase;
-    if (r < r_end) {
-      const int j = r / a.T;
-      const int t = r - j * a.T;
-      const int sl = slots[j];
-      if (sl >= 0 && sl < a.slots_total) {
-        valid = true;
-        rowp = cbase + (int64_t)sl * a.row_bytes + (int64_t)t * (2 * kMlaDqk);
-      }
-    }
-    bf16x8 kf[kKSteps];
+  // this lane's row of a tile (A-operand row m = lane & 15): its slot
+  // (-1 when outside the split or padding), then all of its 16-byte fragments
+  auto row_slot = [&](int tile0) {
+    const int r = tile0 + 16 * wave + (lane & 15);
+    if (tile0 >= r_end || r >= r_end) return -1;
+    const int sl = slots[r / a.T];
+    return (sl >= 0 && sl < a.slots_total) ? sl : -1;
+  };
+  bf16x8 kf[kKSteps];
+  bool valid = false;
+  auto load_rows = [&](int tile0, int sl) {
+    valid = sl >= 0;
+    const int r = tile0 + 16 * wave + (lane & 15);
+    const uint8_t* rowp =
+        cbase + (int64_t)(valid ? sl : 0) * a.row_bytes + (int64_t)(r % a.T) * (2 * kMlaDqk);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
       kf[ks] = valid ? __builtin_nontemporal_load(
                            reinterpret_cast<const bf16x8*>(rowp + 2 * (32 * ks + 8 * g)))
                      : zero8;
-    // value dims [0, 512) of the 16 rows into the wave's LDS buffer
+  };
+
+  // the first tile's rows are requested with the queries; each later tile's
+  // rows while the previous tile is finished (software pipeline)
+  load_rows(r_begin, row_slot(r_begin));
+  // B-operand fragments of Q^T: head h, dims 32 ks + 8 g .. +7
+  bf16x8 qf[kKSteps];
+  {
+    const __bf16* qh = a.q + ((int64_t)b * a.H + hb * kMlaHB + h) * kMlaDqk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * ks);
+  }
+  float m_run = -INFINITY, l_run = 0.f;  // m_run: the workgroup's; l_run: this wave's rows
+  float4_t acc[kWaveDB];
+#pragma unroll
+  for (int db = 0; db < kWaveDB; ++db) acc[db] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int tile0 = r_begin; tile0 < r_end; tile0 += kTile) {
+    const int sl_next = row_slot(tile0 + kTile);
+    const bool valid_now = valid;
+    // value dims [0, 512) of this wave's 16 rows into the tile
 #pragma unroll
     for (int ks = 0; ks < kMlaDv / 32; ++ks)
-      *reinterpret_cast<bf16x8*>(vb + (lane & 15) * kVRowPitch + 32 * ks + 8 * g) = kf[ks];
-
-    // S^T[i][h] for rows i = 4g + j of the tile; Q^T fragments from LDS
+      *reinterpret_cast<bf16x8*>(vt + (16 * wave + (lane & 15)) * kVRowPitch + 32 * ks + 8 * g) =
+          kf[ks];
+    // S^T[i][h] for rows i = 4g + j of the wave's 16
     float4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8 qf = *reinterpret_cast<const bf16x8*>(qs + h * kMlaDqk + 32 * ks + 8 * g);
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf, st, 0, 0, 0);
-    }
-
+    for (int ks = 0; ks < kKSteps; ++ks)
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+    // the fragments are consumed: request the next tile's rows
+    if (tile0 + kTile < r_end) load_rows(tile0 + kTile, sl_next);
     float sc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int vj = __shfl(valid ? 1 : 0, 4 * g + j);
+      const int vj = __shfl(valid_now ? 1 : 0, 4 * g + j);
       sc[j] = vj ? st[j] * a.scale : -INFINITY;
     }
     float tm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     tm = fmaxf(tm, __shfl_xor(tm, 16));
     tm = fmaxf(tm, __shfl_xor(tm, 32));
-    const float m_new = fmaxf(m_run, tm);
+    if (g == 0) red_m[wave * kMlaHB + h] = tm;
+    lds_barrier();  // A: tile maxima (and the V tile) written
+    float m_tile = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMlaWaves; ++w) m_tile = fmaxf(m_tile, red_m[w * kMlaHB + h]);
+    const float m_new = fmaxf(m_run, m_tile);
     float p[4], alpha;
     if (m_new == -INFINITY) {
       alpha = 1.f;
@@ -161,12 +184,7 @@ __global__ void __launch_bounds__(kMlaThreads) mla_decode_kernel(MlaArgs a) {
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
     m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) acc[db] *= alpha;
-    }
-
-    // P^T as the B operand (k = rows 4g..4g+3, n = head), split hi + lo
+    // P^T of the wave's rows 4g .. 4g+3 for head h: four consecutive entries
     short4_t phi, plo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -175,61 +193,46 @@ __global__ void __launch_bounds__(kMlaThreads) mla_decode_kernel(MlaArgs a) {
       phi[j] = bf16_bits(hi);
       plo[j] = bf16_bits(lo);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");  // V tile written
+    *reinterpret_cast<short4_t*>(phi_t + h * kTile + 16 * wave + 4 * g) = phi;
+    *reinterpret_cast<short4_t*>(plo_t + h * kTile + 16 * wave + 4 * g) = plo;
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db) {
-      short4_t va;  // A operand: V^T[d = 16 db + (lane & 15)][rows 4g..4g+3]
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        va[t] = bf16_bits(vb[(4 * g + t) * kVRowPitch + 16 * db + (lane & 15)]);
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, phi, acc[db], 0, 0, 0);
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plo, acc[db], 0, 0, 0);
+      for (int db = 0; db < kWaveDB; ++db) acc[db] *= alpha;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");  // V tile consumed
+    lds_barrier();  // B: P tile written
+    // O^T[128 wave + 16 db + 4g + j][h] += sum over the tile's 64 rows
+#pragma unroll 2
+    for (int rg = 0; rg < kMlaWaves; ++rg) {
+      const short4_t bh = *reinterpret_cast<const short4_t*>(phi_t + h * kTile + 16 * rg + 4 * g);
+      const short4_t bl = *reinterpret_cast<const short4_t*>(plo_t + h * kTile + 16 * rg + 4 * g);
+#pragma unroll
+      for (int db = 0; db < kWaveDB; ++db) {
+        short4_t va;  // A operand: V^T[d = 128 wave + 16 db + (lane & 15)][rows 4g .. 4g+3]
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          va[t] = bf16_bits(
+              vt[(16 * rg + 4 * g + t) * kVRowPitch + 16 * (kWaveDB * wave + db) + (lane & 15)]);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bh, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bl, acc[db], 0, 0, 0);
+      }
+    }
+    lds_barrier();  // C: the tile buffers are free for the next tile
   }
 
-  // ---- combine the waves: common max, then a fixed-order tree in LDS -------
-  if (g == 0) {
-    wml[(wave * kMlaHB + h) * 2 + 0] = m_run;
-    wml[(wave * kMlaHB + h) * 2 + 1] = l_run;
-  }
-  __syncthreads();  // also: every wave is done with its V tile
-  float m_wg = -INFINITY, l_wg = 0.f;
+  // ---- softmax sums of the waves; the partial result --------------------------
+  if (g == 0) red_l[wave * kMlaHB + h] = l_run;
+  lds_barrier();
+  float l_wg = 0.f;
 #pragma unroll
-  for (int w = 0; w < kMlaWaves; ++w) m_wg = fmaxf(m_wg, wml[(w * kMlaHB + h) * 2]);
+  for (int w = 0; w < kMlaWaves; ++w) l_wg += red_l[w * kMlaHB + h];
+  const int pid = (b * a.HBn + hb) * a.S + split;
+  float* part = a.part + (int64_t)pid * kMlaHB * kMlaDv;
 #pragma unroll
-  for (int w = 0; w < kMlaWaves; ++w) {
-    const float mw = wml[(w * kMlaHB + h) * 2];
-    if (mw != -INFINITY) l_wg += expf(mw - m_wg) * wml[(w * kMlaHB + h) * 2 + 1];
-  }
-  const float fac = (m_run == -INFINITY) ? 0.f : expf(m_run - m_wg);
-#pragma unroll
-  for (int db = 0; db < kDBlocks; ++db) acc[db] *= fac;
-  for (int half = kMlaWaves / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
-      float4_t* dst = reinterpret_cast<float4_t*>(tree + (wave - half) * kMlaHB * kMlaDv);
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) dst[db * 64 + lane] = acc[db];
-    }
-    __syncthreads();
-    if (wave < half) {
-      const float4_t* src = reinterpret_cast<const float4_t*>(tree + wave * kMlaHB * kMlaDv);
-#pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) acc[db] += src[db * 64 + lane];
-    }
-    __syncthreads();
-  }
-
-  // ---- wave 0 writes the split's partial result ------------------------------
-  if (wave == 0) {
-    const int pid = (b * a.HBn + hb) * a.S + split;
-    float* part = a.part + (int64_t)pid * kMlaHB * kMlaDv;
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db) reinterpret_cast<float4_t*>(part)[db * 64 + lane] = acc[db];
-    if (g == 0) {
-      a.part_ml[(int64_t)pid * kMlaHB * 2 + h * 2 + 0] = m_wg;
-      a.part_ml[(int64_t)pid * kMlaHB * 2 + h * 2 + 1] = l_wg;
-    }
+  for (int db = 0; db < kWaveDB; ++db)
+    reinterpret_cast<float4_t*>(part)[(kWaveDB * wave + db) * 64 + lane] = acc[db];
+  if (wave == 0 && g == 0) {
+    a.part_ml[(int64_t)pid * kMlaHB * 2 + h * 2 + 0] = m_run;
+    a.part_ml[(int64_t)pid * kMlaHB * 2 + h * 2 + 1] = l_wg;
   }
 }
 
@@ -287,13 +290,18 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaArgs a) {
 }  // namespace
 
 MlaShape mla_shape(int B, int H, int k, int T) {
-  // About one workgroup per CU (256 CUs), each covering whole 128-row tiles
-  // (8 waves x 16 rows, all in flight at once).
+  // Whole 64-row tiles (4 waves x 16 rows, all in flight at once) per
+  // split.  Every split costs a 32 KiB partial written and read back by the
+  // merge, so two workgroups per CU (256 CUs) are used only while a split
+  // keeps at least kMinRows rows (partials <= ~22 % of the row bytes);
+  // otherwise one per CU.
+  constexpr int kMinRows = 256;
   MlaShape s{};
   s.HBn = H / kMlaHB;
   const int n_tok = k * T;
   const int tile = 16 * kMlaWaves;
-  int S = (256 + B * s.HBn - 1) / (B * s.HBn);
+  int S = (256 * kWgPerCu + B * s.HBn - 1) / (B * s.HBn);
+  if (S > 1 && n_tok / S < kMinRows) S = (256 + B * s.HBn - 1) / (B * s.HBn);
   const int max_s = (n_tok + tile - 1) / tile;
   if (S > max_s) S = max_s;
   if (S > kMlaMaxSplits) S = kMlaMaxSplits;
@@ -303,14 +311,16 @@ MlaShape mla_shape(int B, int H, int k, int T) {
   s.rows_per_split = rows;
   s.S = (n_tok + rows - 1) / rows;
   if (s.S < 1) s.S = 1;
-  s.lds_bytes = kMlaVbufBytes + kMlaQBytes + sizeof(float) * kMlaWaves * kMlaHB * 2;
+  s.lds_bytes = kMlaVbufBytes + kMlaPBytes + kMlaRedBytes;
   s.part_floats = (size_t)B * s.HBn * s.S * kMlaHB * kMlaDv;
   s.ml_floats = (size_t)B * s.HBn * s.S * kMlaHB * 2;
   s.counters = 0;
   return s;
 }
 
-hipError_t launch_mla(const MlaArgs& a, hipStream_t s, size_t lds_bytes, int grid) {
+hipError_t launch_mla(const MlaArgs& a, hipStream_t s, size_t lds_bytes) {
+  const int units = a.B * a.S;
+  const int grid = (units + kXcds - 1) / kXcds * kXcds * a.HBn;
   hipLaunchKernelGGL(mla_decode_kernel, dim3(grid), dim3(kMlaThreads), lds_bytes, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -574,7 +574,7 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
   a.part_ml = reinterpret_cast<float*>(w + ws.ml);
   a.out = out;
   a.lse = lse;
-  HIP_TRY(launch_mla(a, stream, sh.lds_bytes, B * sh.HBn * sh.S));
+  HIP_TRY(launch_mla(a, stream, sh.lds_bytes));
   return HISPARSE_OK;
 }
 
