@@ -42,7 +42,9 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: the workload's own step count, 64 for workload 2)")
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2)")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="workload 1..5 of workload/configs.py (default 2: 8 requests, 1 layer, "
+                         "131072 token rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the link-peak probe")
     ap.add_argument("--only-timed", action="store_true",
@@ -281,7 +283,7 @@ def summarize_rocprof(directory, label, command):
     print(out)
 
 
-def committed_traffic(kernel, cfg_name, mode):
+def committed_traffic(kernel, label, mode):
     """HBM+link bytes per launch of `kernel` from the committed PMC summaries
     (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, each scaled by the counter's
     reading for a device copy of known size), or None when absent or taken on
@@ -290,7 +292,7 @@ def committed_traffic(kernel, cfg_name, mode):
     vals = {}
     sha = kernel_source_sha()
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        path = os.path.join(PROFILES, f"pmc_{counter.lower()}_{cfg_name}_{mode}.md")
+        path = os.path.join(PROFILES, f"pmc_{counter.lower()}_{label}_{mode}.md")
         if not os.path.exists(path):
             return None
         text = open(path).read()
@@ -597,10 +599,10 @@ def main():
         sys.exit(2)
     import torch
     from hierarchical_kv_cache_hisparse_amd import binding as hb
-    from workload import CONFIGS
+    from workload import WORKLOADS
 
     torch.cuda.set_device(0)
-    base = CONFIGS[args.config]
+    base = WORKLOADS[args.workload]
     if args.steps is None:
         args.steps = base.steps
     if args.topk:
@@ -681,7 +683,7 @@ def main():
         meta_bytes = cfg.B * (12 * cfg.k + 16 * cfg.C + 4 * (avg_hit + avg_miss) + 24 * avg_miss + 64)
         resolve_gbps = meta_bytes / resolve_avg_s / 1e9 if resolve_avg_s > 0 else 0.0
         dominant = "resolve_kernel" if fused else "fetch_kernel"
-        traffic = committed_traffic(dominant, f"cfg{args.config}", "fused" if fused else "split")
+        traffic = committed_traffic(dominant, cfg.label, "fused" if fused else "split")
 
         result = {
             "metric": "resolved top-k entries/s; miss-fetch GB/s vs host-link peak; no-IO overhead",

@@ -8,7 +8,7 @@ import re
 import pytest
 
 from hierarchical_kv_cache_hisparse_amd import binding as hb
-from workload import CONFIGS
+from workload import WORKLOADS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hisparse.h")
@@ -43,7 +43,7 @@ def _cfg(w, flags=0):
 
 @pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
 def test_workspace_sizes_of_the_workloads(cfg_id):
-    w = CONFIGS[cfg_id]
+    w = WORKLOADS[cfg_id]
     cache, meta = hb.hisparse_workspace_bytes(_cfg(w))
     assert cache == w.layers * w.B * (w.C + w.R) * w.row_bytes
     lay = hb.hisparse_meta_layout_of(_cfg(w))
@@ -72,7 +72,7 @@ def test_workspace_sizes_of_the_workloads(cfg_id):
     ("cache_slots", 20000, hb.HISPARSE_ERR_UNSUPPORTED),
 ])
 def test_invalid_configs_are_rejected_on_the_host(field, value, code):
-    cfg = _cfg(CONFIGS[2])
+    cfg = _cfg(WORKLOADS[2])
     setattr(cfg, field, value)
     with pytest.raises(hb.HisparseError) as e:
         hb.hisparse_workspace_bytes(cfg)
@@ -98,7 +98,7 @@ def test_error_strings():
 
 
 def test_create_rejects_null_and_host_pointers_without_touching_them():
-    cfg = _cfg(CONFIGS[1])
+    cfg = _cfg(WORKLOADS[1])
     with pytest.raises(hb.HisparseError) as e:
         hb.hisparse_create(cfg, [None], 0, 0)
     assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG

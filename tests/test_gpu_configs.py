@@ -11,7 +11,7 @@ workloads also check that every layer of a request stays identical.
 import numpy as np
 import pytest
 
-from workload import CONFIGS
+from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -27,7 +27,7 @@ SAMPLED = {
 def _run_full(cfg_id, flags=0):
     import torch
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     print(f"[full] {cfg.name} flags={flags}: building inputs", flush=True)
     run = LockstepRun(cfg, oracle_streams=SAMPLED[cfg_id], flags=flags)
     checkpoints = {0, cfg.steps // 2, cfg.steps - 1}

@@ -16,7 +16,7 @@ below ~2^-16 * E|v| ~ 1.2e-5.  We allow 5e-5 absolute on out and 2e-5 on lse.
 import numpy as np
 import pytest
 
-from workload import CONFIGS
+from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -95,19 +95,19 @@ def _run(cfg, H, steps=None, requests=None):
 
 @pytest.mark.parametrize("H", [16, 48])
 def test_attention_over_token_slots(H):
-    cfg = CONFIGS[2].scaled(B=3, L0=8192, C=1500, k=700, steps=3)
+    cfg = WORKLOADS[2].scaled(B=3, L0=8192, C=1500, k=700, steps=3)
     _run(cfg, H)
 
 
 def test_attention_over_page_slots():
-    cfg = CONFIGS[5].scaled(B=2, layers=2, L0=3000, C=64, k=40, steps=3)
+    cfg = WORKLOADS[5].scaled(B=2, layers=2, L0=3000, C=64, k=40, steps=3)
     _run(cfg, 16)
 
 
 def test_attention_full_shared_selection_step():
     """The 16-request, 2048-selection shape of the shared-selection workload
     (one layer), 128 heads, sampled requests."""
-    cfg = CONFIGS[4].scaled(layers=1, steps=2)
+    cfg = WORKLOADS[4].scaled(layers=1, steps=2)
     _run(cfg, 128, requests=[0, 7, 15])
 
 
@@ -115,7 +115,7 @@ def test_attention_skips_padding_and_empty_rows():
     import torch
     from hierarchical_kv_cache_hisparse_amd import binding as hb
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[2].scaled(B=3, L0=4000, C=512, k=200, steps=1)
+    cfg = WORKLOADS[2].scaled(B=3, L0=4000, C=512, k=200, steps=1)
     run = LockstepRun(cfg, oracle_streams=[])
     attn = Attn(run, 16)
     try:
@@ -140,7 +140,7 @@ def test_attention_graph_replays_are_bit_reproducible():
     eager work in between: every replay equals the eager launch bit for bit."""
     import torch
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[2].scaled(B=4, L0=6000, C=1024, k=512, steps=1)
+    cfg = WORKLOADS[2].scaled(B=4, L0=6000, C=1024, k=512, steps=1)
     run = LockstepRun(cfg, oracle_streams=[])
     attn = Attn(run, 32)
     try:

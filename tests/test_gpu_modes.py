@@ -11,7 +11,7 @@
 import numpy as np
 import pytest
 
-from workload import CONFIGS
+from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_graph_replay_equals_eager():
     replayed every step, with eager copies and synchronizations in between;
     every replay must equal an eager instance bit for bit."""
     torch, hb = _torch(), _hb()
-    cfg = CONFIGS[3].scaled(B=3, layers=2, L0=9000, C=2048, k=1024, steps=8)
+    cfg = WORKLOADS[3].scaled(B=3, layers=2, L0=9000, C=2048, k=1024, steps=8)
     a, b, trace = _pair(cfg)
     try:
         dev = "cuda:0"
@@ -114,7 +114,7 @@ def test_prefetch_equals_no_prefetch(captured):
     stream (forked after layer l) must give the same slot maps and state as
     resolving every layer in order on one stream."""
     torch, hb = _torch(), _hb()
-    cfg = CONFIGS[4].scaled(B=2, layers=4, L0=30000, steps=6)
+    cfg = WORKLOADS[4].scaled(B=2, layers=4, L0=30000, steps=6)
     a, b, trace = _pair(cfg)
     try:
         dev = "cuda:0"
@@ -171,7 +171,7 @@ def test_prefetch_equals_no_prefetch(captured):
 
 def test_prefetch_misuse_is_reported():
     torch, hb = _torch(), _hb()
-    cfg = CONFIGS[4].scaled(B=2, layers=2, L0=5000, steps=2)
+    cfg = WORKLOADS[4].scaled(B=2, layers=2, L0=5000, steps=2)
     from tests.gpu_harness import GpuInstance
     g = GpuInstance(cfg)
     try:
@@ -197,7 +197,7 @@ def test_prefetch_misuse_is_reported():
 
 def test_no_io_equals_io_metadata_and_reads_nothing():
     torch, hb = _torch(), _hb()
-    cfg = CONFIGS[2].scaled(B=4, L0=20000, steps=10)
+    cfg = WORKLOADS[2].scaled(B=4, L0=20000, steps=10)
     a, b, trace = _pair(cfg, 0, hb.HISPARSE_NO_IO)
     try:
         dev = "cuda:0"
@@ -234,7 +234,7 @@ def test_hits_read_no_host_bytes(noncoherent):
     match the oracle reading the same (poisoned) host memory."""
     torch, hb = _torch(), _hb()
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[2].scaled(B=2, L0=12000, C=1024, k=512, steps=10)
+    cfg = WORKLOADS[2].scaled(B=2, L0=12000, C=1024, k=512, steps=10)
     flags = hb.HISPARSE_HOST_NONCOHERENT if noncoherent else hb.HISPARSE_HOST_COHERENT
     run = LockstepRun(cfg, host_flags=flags)
     try:
@@ -262,7 +262,7 @@ def test_hits_read_no_host_bytes(noncoherent):
 def test_invalid_rows_are_rejected_per_request():
     torch, hb = _torch(), _hb()
     from tests.gpu_harness import GpuInstance
-    cfg = CONFIGS[2].scaled(B=3, L0=6000, C=512, k=256, steps=1)
+    cfg = WORKLOADS[2].scaled(B=3, L0=6000, C=512, k=256, steps=1)
     for flags in (0, hb.HISPARSE_DEBUG_VALIDATE):
         g = GpuInstance(cfg, flags=flags)
         try:
@@ -311,7 +311,7 @@ def test_invalid_rows_are_rejected_per_request():
 def test_snapshot_restore_replays_identically():
     torch, hb = _torch(), _hb()
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[2].scaled(B=2, L0=15000, steps=12)
+    cfg = WORKLOADS[2].scaled(B=2, L0=15000, steps=12)
     run = LockstepRun(cfg)
     try:
         for s in range(5):
@@ -340,7 +340,7 @@ def test_reset_one_request_leaves_the_others():
     torch, hb = _torch(), _hb()
     from oracle.oracle import OracleStream
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[3].scaled(B=3, layers=2, L0=8000, C=1024, k=512, steps=8, growth=0)
+    cfg = WORKLOADS[3].scaled(B=3, layers=2, L0=8000, C=1024, k=512, steps=8, growth=0)
     run = LockstepRun(cfg)
     try:
         for s in range(4):
@@ -367,7 +367,7 @@ def test_reset_one_request_leaves_the_others():
 def test_timing_counts_every_launch():
     torch, hb = _torch(), _hb()
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[3].scaled(B=2, layers=3, L0=5000, C=1024, k=512, steps=4, growth=0)
+    cfg = WORKLOADS[3].scaled(B=2, layers=3, L0=5000, C=1024, k=512, steps=4, growth=0)
     run = LockstepRun(cfg, oracle_streams=[])
     try:
         hb.hisparse_set_timing(run.gpu.h, True)

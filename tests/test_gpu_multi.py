@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from tests import pins
-from workload import CONFIGS
+from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -45,27 +45,27 @@ CASES = {
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_multi_parity(name):
     base, q, kw = CASES[name]
-    _run(CONFIGS[base].scaled(**kw), q)
+    _run(WORKLOADS[base].scaled(**kw), q)
 
 
 @pytest.mark.parametrize("mode", ["fused", "split"])
 def test_multi_parity_fetch_modes(mode, monkeypatch):
     monkeypatch.setenv("HISPARSE_FETCH_MODE", mode)
     base, q, kw = CASES["four_tokens_growth_layers"]
-    _run(CONFIGS[base].scaled(**kw), q)
+    _run(WORKLOADS[base].scaled(**kw), q)
 
 
 def test_multi_parity_no_io():
     from hierarchical_kv_cache_hisparse_amd import binding as hb
     base, q, kw = CASES["two_tokens_window"]
-    _run(CONFIGS[base].scaled(**kw), q, flags=hb.HISPARSE_NO_IO)
+    _run(WORKLOADS[base].scaled(**kw), q, flags=hb.HISPARSE_NO_IO)
 
 
 def test_multi_full_size_two_tokens():
     """Two query tokens of 2048 selections each on the 16-request, 6144-slot
     shape of the independent-layers workload (two layers, sampled streams):
     the 4096-entry rows use the largest deduplication table."""
-    cfg = CONFIGS[3].scaled(layers=2, k=4096, steps=4)
+    cfg = WORKLOADS[3].scaled(layers=2, k=4096, steps=4)
     _run(cfg, 2, oracle_streams=[(0, 0), (7, 1), (15, 0)])
 
 
@@ -124,7 +124,7 @@ def test_multi_graph_replay_equals_eager():
     import torch
     from hierarchical_kv_cache_hisparse_amd import binding as hb
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[2].scaled(B=3, L0=8192, C=1500, k=1200, steps=6)
+    cfg = WORKLOADS[2].scaled(B=3, L0=8192, C=1500, k=1200, steps=6)
     Q = 3
     run = LockstepRun(cfg, queries=Q)
     try:
@@ -159,7 +159,7 @@ def test_multi_rejects_bad_rows_per_request():
     import torch
     from hierarchical_kv_cache_hisparse_amd import binding as hb
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[2].scaled(B=3, L0=6000, C=800, k=400, steps=2)
+    cfg = WORKLOADS[2].scaled(B=3, L0=6000, C=800, k=400, steps=2)
     Q = 2
     run = LockstepRun(cfg, queries=Q)
     try:
@@ -192,7 +192,7 @@ def test_multi_argument_checks():
     import torch
     from hierarchical_kv_cache_hisparse_amd import binding as hb
     from tests.gpu_harness import GpuInstance
-    cfg = CONFIGS[4].scaled(B=2, layers=2, L0=5000, C=512, R=8, k=256, steps=1)
+    cfg = WORKLOADS[4].scaled(B=2, layers=2, L0=5000, C=512, R=8, k=256, steps=1)
     g = GpuInstance(cfg)
     try:
         sel = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from tests import pins
-from workload import CONFIGS
+from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_parity_fetch_modes(name, mode, monkeypatch):
 
 
 def _parity_case(name, base, kw):
-    cfg = CONFIGS[base].scaled(**kw)
+    cfg = WORKLOADS[base].scaled(**kw)
     print(f"[parity] {name}: B={cfg.B} L={cfg.layers} L0={cfg.L0} C={cfg.C} R={cfg.R} "
           f"k={cfg.k} steps={cfg.steps}", flush=True)
     _run_lockstep(cfg)
@@ -68,7 +68,7 @@ def _parity_case(name, base, kw):
 @pytest.mark.parametrize("name", ["mix_window_two_rounds", "pages"])
 def test_parity_reduced_no_io(name):
     base, kw = CASES[name]
-    cfg = CONFIGS[base].scaled(**kw)
+    cfg = WORKLOADS[base].scaled(**kw)
     from hierarchical_kv_cache_hisparse_amd import binding as hb
     _run_lockstep(cfg, flags=hb.HISPARSE_NO_IO)
 

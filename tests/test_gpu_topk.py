@@ -7,7 +7,7 @@ replay, and the selection fed straight into the resolver."""
 import numpy as np
 import pytest
 
-from workload import CONFIGS
+from workload import WORKLOADS
 
 pytestmark = pytest.mark.gpu
 
@@ -134,7 +134,7 @@ def test_topk_workspace_reuse_and_graph_replay():
 def test_topk_full_layer_shapes(cfg_id):
     """One layer call at the workload's shape: 16 x 131072 tokens (k 2048),
     16 x 262144 tokens (k 2048), 4 x 65536 pages (k 128)."""
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     print(f"[topk] full shape {cfg.name}: rows={cfg.B} n={cfg.L0} k={cfg.k}", flush=True)
     t = Topk(cfg.B, cfg.L0)
     s = _scores(cfg.B, cfg.L0, 4400 + cfg_id, ties=True)
@@ -148,7 +148,7 @@ def test_topk_feeds_the_resolver():
     from hierarchical_kv_cache_hisparse_amd import binding as hb
     from oracle.topk import topk_rows
     from tests.gpu_harness import LockstepRun
-    cfg = CONFIGS[2].scaled(B=3, L0=12000, C=1500, k=600, steps=6)
+    cfg = WORKLOADS[2].scaled(B=3, L0=12000, C=1500, k=600, steps=6)
     run = LockstepRun(cfg, fill_all=True)
     t = Topk(cfg.B, cfg.L0)
     try:

@@ -14,11 +14,11 @@ import pytest
 
 from oracle.attention import bf16_to_f64, mla_decode_attention, masked_dense_attention
 from tests.harness import OracleRun, fill_host, make_trace, small_variant
-from workload import CONFIGS
+from workload import WORKLOADS
 
 
 def _small(cfg_id):
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     if cfg.row_elems > 576:   # page rows
         return small_variant(cfg, B=2, layers=2, L0=2048, C=64, k=32, steps=12)
     return small_variant(cfg, B=2, layers=2, L0=8192, C=768, k=384, steps=10)
@@ -77,7 +77,7 @@ def test_attention_through_slot_map_is_unchanged():
     rows at the selected positions bit for bit (same bytes, same order), and a
     masked dense attention over the whole history in position order agrees to
     rounding (float64, relative 1e-12)."""
-    cfg = small_variant(CONFIGS[2], B=1, layers=1, L0=4096, C=512, k=256, steps=6)
+    cfg = small_variant(WORKLOADS[2], B=1, layers=1, L0=4096, C=512, k=256, steps=6)
     streams = [(0, 0)]
     trace = make_trace(cfg)
     host = np.zeros((cfg.l_cap, cfg.row_bytes), np.uint8)

@@ -5,7 +5,7 @@ import pytest
 
 from oracle.oracle import OracleStream
 from tests import pins
-from workload import CONFIGS
+from workload import WORKLOADS
 from workload.traces import stream_trace
 
 
@@ -27,7 +27,7 @@ def test_no_eviction_closed_form_config1():
     n-th distinct position (in step, then selection order) takes slot n-1 and
     nothing is evicted.  The 1-request workload (C=4096, k=2048, 8 steps, 90%
     carry-over) is such a case."""
-    cfg = CONFIGS[1]
+    cfg = WORKLOADS[1]
     trace = stream_trace(cfg, 0, 0)
     st = OracleStream(cfg.C, cfg.R, cfg.l_cap, cfg.row_bytes)
     first_seen = {}
@@ -97,7 +97,7 @@ def test_window_covering_context_is_all_resident():
 def test_config_step0_fills_free_slots_in_order(cfg_id):
     """Closed form for the first step of every workload: all non-resident
     selections miss and take free slots 0, 1, 2, ... in selection order."""
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     trace = stream_trace(cfg, 0, 0, steps=1)
     st = OracleStream(cfg.C, cfg.R, cfg.l_cap, cfg.row_bytes)
     r = st.resolve(trace[0], cfg.ctx_at(0))

@@ -4,14 +4,14 @@ row generator is deterministic, subset-consistent and N(0,1)-distributed
 import numpy as np
 import pytest
 
-from workload import CONFIGS
+from workload import WORKLOADS
 from workload import rows as wrows
 from workload.traces import full_trace, stream_trace, touched_positions
 
 
 @pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
 def test_trace_structure(cfg_id):
-    cfg = CONFIGS[cfg_id]
+    cfg = WORKLOADS[cfg_id]
     tr = stream_trace(cfg, 0, 0)
     assert tr.shape == (cfg.steps, cfg.k) and tr.dtype == np.int32
     for s in range(cfg.steps):
@@ -25,20 +25,20 @@ def test_trace_structure(cfg_id):
 
 
 def test_carry_counts_match_the_stated_fractions():
-    assert [CONFIGS[c].n_keep for c in (1, 2, 3, 4, 5)] == [1843, 1740, 1638, 1536, 89]
+    assert [WORKLOADS[c].n_keep for c in (1, 2, 3, 4, 5)] == [1843, 1740, 1638, 1536, 89]
 
 
 def test_shared_and_independent_layers():
-    cfg4 = CONFIGS[4].scaled(steps=3, B=2)
+    cfg4 = WORKLOADS[4].scaled(steps=3, B=2)
     t4 = full_trace(cfg4)
     assert all(np.array_equal(t4[:, 0], t4[:, l]) for l in range(cfg4.layers))
-    cfg3 = CONFIGS[3].scaled(steps=3, B=2, layers=3)
+    cfg3 = WORKLOADS[3].scaled(steps=3, B=2, layers=3)
     t3 = full_trace(cfg3)
     assert not np.array_equal(t3[:, 0], t3[:, 1])
 
 
 def test_zipf_replacements_favour_recent_positions():
-    cfg = CONFIGS[4].scaled(steps=8)
+    cfg = WORKLOADS[4].scaled(steps=8)
     tr = stream_trace(cfg, 0, 0)
     dist = cfg.L0 - tr[1:].astype(np.int64)
     # uniform would put ~1.6% of the positions within 4096 of the end; Zipf(1.0)
@@ -47,7 +47,7 @@ def test_zipf_replacements_favour_recent_positions():
 
 
 def test_mix_replacements_are_half_uniform():
-    cfg = CONFIGS[2].scaled(steps=6)
+    cfg = WORKLOADS[2].scaled(steps=6)
     tr = stream_trace(cfg, 0, 0)
     far = np.mean(cfg.L0 - tr[0].astype(np.int64) > cfg.L0 // 2)
     # the uniform half lands in the older half about half the time (~25%);
@@ -56,7 +56,7 @@ def test_mix_replacements_are_half_uniform():
 
 
 def test_growth_workload_uses_current_context():
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS[3]
     assert cfg.l_cap == 131072 + 31
     assert cfg.ctx_at(31) == 131103
 
@@ -89,7 +89,7 @@ def test_row_values_are_standard_normal_bf16():
 
 
 def test_touched_positions_cover_window_and_selections():
-    cfg = CONFIGS[2].scaled(steps=3)
+    cfg = WORKLOADS[2].scaled(steps=3)
     tr = stream_trace(cfg, 0, 0)
     pos = touched_positions(tr, cfg)
     assert set(np.unique(tr).tolist()) <= set(pos.tolist())

@@ -71,6 +71,17 @@ class Workload:
         return self.k - self.n_keep
 
     @property
+    def label(self) -> str:
+        """Short file-name form of the workload: row kind, requests (x
+        layers), context length."""
+        kind, _, rest = self.name.partition("_")
+        parts = rest.split("_")
+        b = parts[0]
+        l = parts[1]
+        ctx = next(x for x in parts if x.startswith("L") and x[1:2].isdigit())
+        return f"{kind}_{b}{'' if l == 'l1' else 'x' + l[1:]}_{ctx}"
+
+    @property
     def streams(self) -> int:
         return self.B * self.layers
 
@@ -78,9 +89,9 @@ class Workload:
         return replace(self, **kw)
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload(
-        name="cfg1_b1_l1_L32k_C4096_k2048",
+        name="tokens_b1_l1_L32k_C4096_k2048",
         B=1, layers=1, L0=32768, growth=0, row_elems=TOKEN_ROW_ELEMS,
         C=4096, R=0, k=2048, steps=8, carry_pct=90, replacement="uniform",
         trace_seed=1001, data_seed=2001,
@@ -88,7 +99,7 @@ CONFIGS = {
                     "no resident window, k=2048, 8 steps, 90% carry-over, "
                     "uniform replacements"),
     2: Workload(
-        name="cfg2_b8_l1_L128k_C4096_R128_k2048",
+        name="tokens_b8_l1_L128k_C4096_R128_k2048",
         B=8, layers=1, L0=131072, growth=0, row_elems=TOKEN_ROW_ELEMS,
         C=4096, R=128, k=2048, steps=64, carry_pct=85, replacement="mix",
         zipf_s=1.1, trace_seed=1002, data_seed=2002,
@@ -97,7 +108,7 @@ CONFIGS = {
                     "uniform over [0,L-R) and half Zipf(1.1) over distance from "
                     "the context end"),
     3: Workload(
-        name="cfg3_b16_l8_indep_L128k_grow_C6144_R128_k2048",
+        name="tokens_b16_l8_indep_L128k_grow_C6144_R128_k2048",
         B=16, layers=8, L0=131072, growth=1, row_elems=TOKEN_ROW_ELEMS,
         C=6144, R=128, k=2048, steps=32, carry_pct=80, replacement="uniform",
         trace_seed=1003, data_seed=2003,
@@ -106,7 +117,7 @@ CONFIGS = {
                     "step, C=6144, R=128, k=2048, 32 steps, 80% carry-over, "
                     "uniform replacements"),
     4: Workload(
-        name="cfg4_b16_l8_shared_L256k_C4096_R64_k2048",
+        name="tokens_b16_l8_shared_L256k_C4096_R64_k2048",
         B=16, layers=8, L0=262144, growth=0, row_elems=TOKEN_ROW_ELEMS,
         C=4096, R=64, k=2048, steps=32, carry_pct=75, replacement="zipf",
         zipf_s=1.0, shared_selection=True, trace_seed=1004, data_seed=2004,
@@ -115,7 +126,7 @@ CONFIGS = {
                     "carry-over, Zipf(1.0) recency-skewed replacements; the "
                     "next layer is prefetched on a second stream"),
     5: Workload(
-        name="cfg5_b4_l4_pages_L1M_C512_R1_k128",
+        name="pages_b4_l4_L1M_C512_R1_k128",
         B=4, layers=4, L0=65536, growth=0, row_elems=PAGE_ROW_ELEMS,
         C=512, R=1, k=128, steps=64, carry_pct=70, replacement="uniform",
         trace_seed=1005, data_seed=2005,
@@ -126,4 +137,4 @@ CONFIGS = {
 }
 
 # The workload the headline throughput is quoted on (fits one GPU).
-BENCH_CONFIG = 2
+BENCH_WORKLOAD = 2
