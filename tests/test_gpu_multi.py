@@ -39,6 +39,8 @@ CASES = {
     "two_tokens_shared_layers": (4, 2, dict(B=2, layers=2, L0=20000, k=2048, steps=5)),
     "two_tokens_pages": (5, 2, dict(B=2, layers=2, L0=3000, k=128, steps=8)),
     "tiny_cache_many_tokens": (2, 8, dict(B=2, L0=600, C=64, R=3, k=64, steps=12)),
+    # 12 entries per thread, 12000 slots and a 8192-cell deduplication table
+    "largest_shape_two_tokens": (1, 2, dict(L0=60000, C=12000, k=3000, steps=4)),
 }
 
 
@@ -53,6 +55,14 @@ def test_multi_parity_fetch_modes(mode, monkeypatch):
     monkeypatch.setenv("HISPARSE_FETCH_MODE", mode)
     base, q, kw = CASES["four_tokens_growth_layers"]
     _run(WORKLOADS[base].scaled(**kw), q)
+
+
+def test_multi_parity_debug_validate():
+    """Repeated positions are the point of a multi-query row: with the debug
+    flag set they must not be reported as duplicates, and parity holds."""
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    base, q, kw = CASES["two_tokens_window"]
+    _run(WORKLOADS[base].scaled(**kw), q, flags=hb.HISPARSE_DEBUG_VALIDATE)
 
 
 def test_multi_parity_no_io():
