@@ -23,14 +23,18 @@
 //     other waits for its rows); a workgroup (4 waves) walks its split in
 //     tiles of 64 rows, each row read once from HBM (16-byte loads, all in
 //     flight, the next tile's requested while the current one is finished);
+//   * rows are read with whole 128-byte lines per request (8 rows x 128
+//     contiguous bytes per load instruction: half-line requests cost a
+//     quarter of the gather bandwidth) into an LDS copy of the tile, from
+//     which both MFMA operands of the rows are read;
 //   * scores: wave w takes rows 16w .. 16w+15 of the tile, S^T (16 rows x 16
-//     heads) = K . Q^T with v_mfma_f32_16x16x32_bf16, row fragments straight
-//     from the slot rows, the 16 query heads' fragments held in registers;
+//     heads) = K . Q^T with v_mfma_f32_16x16x32_bf16, the 16 query heads'
+//     fragments held in registers;
 //   * online softmax in fp32 with one running max per head for the whole
 //     workgroup (the waves exchange their tile maxima through LDS), so every
 //     wave scales its rows the same way;
-//   * values: the tile's V part (512 dims) and P^T (hi and lo bf16 parts,
-//     so the products keep ~16 more bits than a plain bf16 P) go to LDS, and
+//   * values: P^T (hi and lo bf16 parts, so the products keep ~16 more bits
+//     than a plain bf16 P) goes to LDS next to the rows, and
 //     wave w accumulates O^T for output dims 128w .. 128w+127 over the 64 rows
 //     with v_mfma_f32_16x16x16_bf16: the waves own disjoint dims, so nothing
 //     is combined across waves but the softmax sums;
@@ -53,8 +57,9 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKSteps = kMlaDqk / 32;  // 18 steps of 32 dims for the scores
 constexpr int kTile = 16 * kMlaWaves;   // 64 rows per tile
-constexpr int kVRowPitch = kMlaDv + 8;  // bf16 per LDS row (padding against bank conflicts)
-constexpr size_t kMlaVbufBytes = sizeof(uint16_t) * kTile * kVRowPitch;     // 65 KiB
+constexpr int kKRowPitch = kMlaDqk + 8;  // bf16 per LDS row: 1168 B (16-byte aligned, and
+                                         // 16 consecutive rows start on distinct bank quads)
+constexpr size_t kMlaKbufBytes = sizeof(uint16_t) * kTile * kKRowPitch;     // 73 KiB
 constexpr size_t kMlaPBytes = 2 * sizeof(uint16_t) * kMlaHB * kTile;        // 4 KiB (hi, lo)
 constexpr size_t kMlaRedBytes = sizeof(float) * 2 * kMlaWaves * kMlaHB;     // 0.5 KiB
 constexpr int kDBlocks = kMlaDv / 16;                 // 32 blocks of 16 output dims
@@ -67,12 +72,13 @@ __device__ __forceinline__ short bf16_bits(__bf16 x) {
   return __builtin_bit_cast(short, x);
 }
 
-__global__ void __launch_bounds__(kMlaThreads) mla_decode_kernel(MlaArgs a) {
+__global__ void __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+mla_decode_kernel(MlaArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16* vt = reinterpret_cast<__bf16*>(smem);                       // [64][pitch]
-  short* phi_t = reinterpret_cast<short*>(smem + kMlaVbufBytes);       // [16 heads][64]
+  __bf16* kt = reinterpret_cast<__bf16*>(smem);                       // [64 rows][pitch]
+  short* phi_t = reinterpret_cast<short*>(smem + kMlaKbufBytes);       // [16 heads][64]
   short* plo_t = phi_t + kMlaHB * kTile;
-  float* red = reinterpret_cast<float*>(smem + kMlaVbufBytes + kMlaPBytes);
+  float* red = reinterpret_cast<float*>(smem + kMlaKbufBytes + kMlaPBytes);
   float* red_m = red;                      // [waves][16] tile maxima
   float* red_l = red + kMlaWaves * kMlaHB;  // [waves][16] softmax sums
 
@@ -102,31 +108,48 @@ __global__ void __launch_bounds__(kMlaThreads) mla_decode_kernel(MlaArgs a) {
   const uint8_t* cbase = a.cache + (int64_t)b * a.stream_bytes;
   const bf16x8 zero8 = {};
 
-  // this lane's row of a tile (A-operand row m = lane & 15): its slot
-  // (-1 when outside the split or padding), then all of its 16-byte fragments
-  auto row_slot = [&](int tile0) {
-    const int r = tile0 + 16 * wave + (lane & 15);
+  // The wave's 16 rows of a tile are read with whole 128-byte lines per
+  // request: load j (0 .. 17) covers rows 8 (j & 1) + lane / 8, bytes
+  // 128 (j >> 1) + 16 (lane % 8) .. +15 of each, i.e. 8 rows x 128 contiguous
+  // bytes, and goes to the LDS copy of the tile; the MFMA operands are read
+  // from there.  row_slot(tile0, m): slot of the wave's row m, -1 when
+  // outside the split or padding.
+  auto row_slot = [&](int tile0, int m) {
+    const int r = tile0 + 16 * wave + m;
     if (tile0 >= r_end || r >= r_end) return -1;
     const int sl = slots[r / a.T];
     return (sl >= 0 && sl < a.slots_total) ? sl : -1;
   };
   bf16x8 kf[kKSteps];
-  bool valid = false;
-  auto load_rows = [&](int tile0, int sl) {
-    valid = sl >= 0;
-    const int r = tile0 + 16 * wave + (lane & 15);
-    const uint8_t* rowp =
-        cbase + (int64_t)(valid ? sl : 0) * a.row_bytes + (int64_t)(r % a.T) * (2 * kMlaDqk);
+  auto load_rows = [&](int tile0, int sl0, int sl1) {  // rows lane/8 and 8 + lane/8
+    const uint8_t* rp[2];
+    const int sls[2] = {sl0, sl1};
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      kf[ks] = valid ? __builtin_nontemporal_load(
-                           reinterpret_cast<const bf16x8*>(rowp + 2 * (32 * ks + 8 * g)))
-                     : zero8;
+    for (int half = 0; half < 2; ++half) {
+      const int m = 8 * half + (lane >> 3);
+      const int r = tile0 + 16 * wave + m;
+      rp[half] = cbase + (int64_t)(sls[half] >= 0 ? sls[half] : 0) * a.row_bytes +
+                 (int64_t)(r % a.T) * (2 * kMlaDqk) + 16 * (lane & 7);
+    }
+#pragma unroll
+    for (int j = 0; j < kKSteps; ++j)
+      kf[j] = sls[j & 1] >= 0
+                  ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(rp[j & 1] + 128 * (j >> 1)))
+                  : zero8;
+  };
+  auto store_rows = [&]() {  // the loaded lines into the wave's 16 rows of the tile
+#pragma unroll
+    for (int j = 0; j < kKSteps; ++j) {
+      const int m = 8 * (j & 1) + (lane >> 3);
+      *reinterpret_cast<bf16x8*>(kt + (16 * wave + m) * kKRowPitch + 64 * (j >> 1) + 8 * (lane & 7)) =
+          kf[j];
+    }
   };
 
   // the first tile's rows are requested with the queries; each later tile's
   // rows while the previous tile is finished (software pipeline)
-  load_rows(r_begin, row_slot(r_begin));
+  load_rows(r_begin, row_slot(r_begin, lane >> 3), row_slot(r_begin, 8 + (lane >> 3)));
+  bool valid = row_slot(r_begin, lane & 15) >= 0;  // the MFMA row of this lane
   // B-operand fragments of Q^T: head h, dims 32 ks + 8 g .. +7
   bf16x8 qf[kKSteps];
   {
@@ -140,20 +163,25 @@ __global__ void __launch_bounds__(kMlaThreads) mla_decode_kernel(MlaArgs a) {
   for (int db = 0; db < kWaveDB; ++db) acc[db] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int tile0 = r_begin; tile0 < r_end; tile0 += kTile) {
-    const int sl_next = row_slot(tile0 + kTile);
+    const int sl0_next = row_slot(tile0 + kTile, lane >> 3);
+    const int sl1_next = row_slot(tile0 + kTile, 8 + (lane >> 3));
+    const bool valid_next = row_slot(tile0 + kTile, lane & 15) >= 0;
     const bool valid_now = valid;
-    // value dims [0, 512) of this wave's 16 rows into the tile
-#pragma unroll
-    for (int ks = 0; ks < kMlaDv / 32; ++ks)
-      *reinterpret_cast<bf16x8*>(vt + (16 * wave + (lane & 15)) * kVRowPitch + 32 * ks + 8 * g) =
-          kf[ks];
-    // S^T[i][h] for rows i = 4g + j of the wave's 16
+    store_rows();
+    // the registers are free: request the next tile's rows
+    if (tile0 + kTile < r_end) load_rows(tile0 + kTile, sl0_next, sl1_next);
+    valid = valid_next;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // the wave's rows in LDS
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    // S^T[i][h] for rows i = 4g + j of the wave's 16 (A fragments from LDS)
     float4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], st, 0, 0, 0);
-    // the fragments are consumed: request the next tile's rows
-    if (tile0 + kTile < r_end) load_rows(tile0 + kTile, sl_next);
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+          kt + (16 * wave + (lane & 15)) * kKRowPitch + 32 * ks + 8 * g);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[ks], st, 0, 0, 0);
+    }
     float sc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -211,7 +239,7 @@ __global__ void __launch_bounds__(kMlaThreads) mla_decode_kernel(MlaArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           va[t] = bf16_bits(
-              vt[(16 * rg + 4 * g + t) * kVRowPitch + 16 * (kWaveDB * wave + db) + (lane & 15)]);
+              kt[(16 * rg + 4 * g + t) * kKRowPitch + 16 * (kWaveDB * wave + db) + (lane & 15)]);
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bh, acc[db], 0, 0, 0);
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bl, acc[db], 0, 0, 0);
       }
@@ -311,7 +339,7 @@ MlaShape mla_shape(int B, int H, int k, int T) {
   s.rows_per_split = rows;
   s.S = (n_tok + rows - 1) / rows;
   if (s.S < 1) s.S = 1;
-  s.lds_bytes = kMlaVbufBytes + kMlaPBytes + kMlaRedBytes;
+  s.lds_bytes = kMlaKbufBytes + kMlaPBytes + kMlaRedBytes;
   s.part_floats = (size_t)B * s.HBn * s.S * kMlaHB * kMlaDv;
   s.ml_floats = (size_t)B * s.HBn * s.S * kMlaHB * 2;
   s.counters = 0;
