@@ -73,6 +73,11 @@ def parse_args():
     ap.add_argument("--topk", action="store_true",
                     help="time the top-k selection producer over synthetic indexer scores at "
                          "the workload's per-layer shape (requests x context rows, k)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="time the layer step as a DSA-style decode step runs it: indexer scores "
+                         "-> top-k -> resolve with miss fetch -> sparse MLA attention (--heads), "
+                         "every layer, all steps in one HIP graph; also with the copies "
+                         "suppressed")
     ap.add_argument("--queries", type=int, default=1,
                     help="query tokens per request and step (multi-token prediction): each "
                          "brings the workload's k selections; resolved in one pass per layer")
@@ -576,6 +581,88 @@ def capture_steps(setup, inst, K):
     return g
 
 
+def pipeline_study(setup, K, H):
+    """Scores -> top-k -> resolve (+ miss fetch) -> sparse MLA attention for
+    every layer of every step, captured as one HIP graph and replayed once
+    from a cold cache, on the IO instance and on the instance that suppresses
+    the copies.  Scores drift as the indexer's would: per layer a fixed N(0,1)
+    base, plus 0.35 x N(0,1) noise per (step, layer), drawn on the device with
+    a seeded generator before the timed region.  The selections therefore
+    differ from the workload's trace, and host rows outside the trace's are
+    zero: timing only; the pieces are parity-tested separately."""
+    import torch
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    from workload.rows import make_queries
+    cfg = setup.cfg
+    dev = "cuda:0"
+    B, N, k, L = cfg.B, cfg.L0, cfg.k, cfg.layers
+    stride = ((cfg.l_cap + 3) // 4) * 4
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6000 + cfg.data_seed)
+    base = torch.randn((L, B, N), generator=gen, device=dev)
+    scores = torch.zeros((K * L, B, stride), dtype=torch.float32, device=dev)
+    for s in range(K):
+        for l in range(L):
+            scores[s * L + l, :, :N] = base[l] + 0.35 * torch.randn((B, N), generator=gen,
+                                                                     device=dev)
+    del base
+    tk_ws = torch.zeros(hb.hisparse_topk_workspace_bytes(B, cfg.l_cap), dtype=torch.uint8,
+                        device=dev)
+    sel = torch.empty((L, B, k), dtype=torch.int32, device=dev)
+    q = torch.from_numpy(make_queries(B, H, 3000 + cfg.data_seed, 0)).to(dev)
+    att = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    scale = 1.0 / np.sqrt(576.0)
+
+    def run(inst, label):
+        ws = torch.empty(hb.hisparse_mla_workspace_bytes(inst.h, H), dtype=torch.uint8,
+                         device=dev)
+        setup.reset(inst)
+        side = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                st = torch.cuda.current_stream().cuda_stream
+                for s in range(K):
+                    for l in range(L):
+                        if cfg.growth and s > 0:
+                            hb.hisparse_append(inst.h, st, l, setup.rows[s, l].data_ptr(),
+                                               setup.pos[s].data_ptr())
+                        hb.hisparse_topk(st, scores[s * L + l].data_ptr(), stride, B,
+                                         cfg.l_cap, setup.ctx[s].data_ptr(), k, tk_ws.data_ptr(),
+                                         sel[l].data_ptr())
+                        hb.hisparse_resolve(inst.h, st, sel[l].data_ptr(), setup.ctx[s].data_ptr(),
+                                            l, setup.out[l].data_ptr())
+                        hb.hisparse_sparse_mla_decode(inst.h, st, l, q.data_ptr(),
+                                                      setup.out[l].data_ptr(), H, scale,
+                                                      ws.data_ptr(), att.data_ptr(), lse.data_ptr())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        setup.reset(inst)
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        assert inst.status() == 0
+        misses = int(setup.totals(inst)[0])
+        log(f"pipeline {label}: {K} steps x {L} layers in {dt * 1e3:.2f} ms, {misses} misses")
+        return dt, misses
+
+    dt_io, misses = run(setup.io, "IO")
+    dt_noio, _ = run(setup.noio, "no-IO")
+    calls = K * L
+    return {"metric": "decode layer step: indexer top-k -> resolve -> sparse MLA attention",
+            "value": round(dt_io / calls * 1e6, 3), "unit": "us per layer call",
+            "higher_is_better": False, "workload": cfg.name, "heads": H, "steps": K,
+            "layers": L,
+            "no_io_us_per_layer_call": round(dt_noio / calls * 1e6, 3),
+            "miss_bytes_per_layer_call": round(misses * cfg.row_bytes / calls),
+            "miss_fetch_share": round(1.0 - dt_noio / dt_io, 4) if dt_io > 0 else None,
+            "mode": "one HIP graph of all steps and layers, one timed replay from a cold cache",
+            "note": "selections come from top-k over synthetic scores (not the workload trace)"}
+
+
 def cpu_baseline(setup, steps, threads=1, min_seconds=10.0):
     """The CPU oracle (plain C) on the same trace and host rows, repeated from
     a cold state until at least `min_seconds` of wall time are measured.  With
@@ -637,6 +724,12 @@ def main():
     setup = Setup(cfg, host_flags, queries=Q)
     K, W = args.steps, args.warmup
     io = setup.noio if (args.no_io and args.only_timed) else setup.io
+    if args.pipeline:
+        try:
+            print(json.dumps(pipeline_study(setup, K, args.heads)), flush=True)
+        finally:
+            setup.close()
+        return
     if args.mla_attention:
         try:
             print(json.dumps(mla_study(setup, K, args.heads)), flush=True)
