@@ -317,11 +317,12 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
  * not be NaN (a NaN is ordered above +inf).
  *
  * hisparse_topk_workspace_bytes: device workspace for rows of up to max_len
- *   positions: a 16 KiB histogram and a counter per row, a position bitmap
- *   and room for max_len boundary candidates (8 bytes each) per row.  Host
+ *   positions: two 16 KiB histograms (top 12 and next 12 key bits) and a
+ *   few counters per row, a position bitmap and room for max_len boundary
+ *   candidates (8 bytes each) per row.  Host
  *   only.  The workspace must be zero-filled once before its first use;
  *   every call leaves the parts it needs zeroed again.
- * hisparse_topk (async on `stream`, graph-capturable: two launches, no
+ * hisparse_topk (async on `stream`, graph-capturable: three launches, no
  *   memset; calls sharing a workspace must be ordered):
  *   scores:     device fp32, row b at scores + b * row_stride, 16-byte
  *               aligned, row_stride >= max_len and a multiple of 4;
