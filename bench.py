@@ -36,6 +36,7 @@ LINK_PEAK_THEORETICAL_GBPS = 64.0      # PCIe Gen5 x16, per direction
 HBM_PEAK_GBPS = 8000.0                  # MI355X HBM3E
 DECODE_STEP_BUDGET_US = 20000.0         # reading: 20 ms decode step ...
 BUDGET_LAYERS = 64                      # ... spread over a 64-layer model
+NOIO_STEP_BUDGET_US = 1000.0            # whole-step resolution without copies, all layers
 
 
 def parse_args():
@@ -663,11 +664,13 @@ def pipeline_study(setup, K, H):
             "note": "selections come from top-k over synthetic scores (not the workload trace)"}
 
 
-def cpu_baseline(setup, steps, threads=1, min_seconds=10.0):
+def cpu_baseline(setup, steps, threads=1, min_seconds=10.0, no_io_seconds=0.0):
     """The CPU oracle (plain C) on the same trace and host rows, repeated from
     a cold state until at least `min_seconds` of wall time are measured.  With
     threads > 1 the independent streams are spread over that many threads
-    (the C oracle runs without the Python lock)."""
+    (the C oracle runs without the Python lock).  With no_io_seconds > 0 the
+    same trace is also timed with the row copies suppressed, and the copy rate
+    (miss bytes / the time difference) is reported."""
     from concurrent.futures import ThreadPoolExecutor
     from tests.harness import OracleRun
     cfg = setup.cfg
@@ -675,24 +678,52 @@ def cpu_baseline(setup, steps, threads=1, min_seconds=10.0):
     host_of = lambda b, l: setup.hosts[(b, l)][1]
     groups = [streams[i::threads] for i in range(threads)]
 
-    def run_group(group):
+    def run_group(group, no_io):
         run = OracleRun(cfg, group, host_of=host_of)
+        missed = 0
         for s in range(steps):
             if cfg.growth and s > 0:
                 run.append(s)
-            run.step(s, setup.trace, queries=setup.queries)
+            res = run.step(s, setup.trace, no_io=no_io, queries=setup.queries)
+            missed += sum(int(r.counters["n_miss"]) for r in res.values())
+        return missed
 
-    elapsed, entries, reps = 0.0, 0, 0
-    with ThreadPoolExecutor(threads) as pool:
-        while elapsed < min_seconds and reps < 2000:
-            t0 = time.perf_counter()
-            list(pool.map(run_group, groups))
-            elapsed += time.perf_counter() - t0
-            entries += steps * cfg.layers * cfg.B * cfg.k
-            reps += 1
-    return {"value": entries / elapsed, "unit": "entries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} x the full {steps}-step trace of all {len(streams)} streams "
-                      f"with row copies ({elapsed:.1f}s wall, {threads} thread(s))"}
+    def timed(no_io, seconds):
+        elapsed, entries, reps, missed = 0.0, 0, 0, 0
+        with ThreadPoolExecutor(threads) as pool:
+            while elapsed < seconds and reps < 2000:
+                t0 = time.perf_counter()
+                missed += sum(pool.map(lambda g: run_group(g, no_io), groups))
+                elapsed += time.perf_counter() - t0
+                entries += steps * cfg.layers * cfg.B * cfg.k
+                reps += 1
+        return elapsed, entries, reps, missed
+
+    elapsed, entries, reps, missed = timed(False, min_seconds)
+    out = {"value": entries / elapsed, "unit": "entries/s", "cores": threads, "kind": "oracle",
+           "sample": f"{reps} x the full {steps}-step trace of all {len(streams)} streams "
+                     f"with row copies ({elapsed:.1f}s wall, {threads} thread(s))",
+           "cpu_model": cpu_model()}
+    if no_io_seconds > 0:
+        e2, n2, r2, _ = timed(True, no_io_seconds)
+        out["no_io_value"] = n2 / e2
+        out["no_io_sample"] = f"{r2} x the same trace, row copies suppressed ({e2:.1f}s wall)"
+        copy_s = elapsed / reps - e2 / r2
+        out["memcpy_GBps"] = (round(missed / reps * cfg.row_bytes / copy_s / 1e9, 3)
+                              if copy_s > 0 else None)
+    return out
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -927,13 +958,41 @@ def main():
             io_minus_noio = dt_io - dt_noio
             result["miss_fetch"]["GBps_io_minus_noio"] = round(
                 miss_bytes / io_minus_noio / 1e9, 3) if io_minus_noio > 0 else None
+            result["no_io"]["us_per_step"] = round(dt_noio / K * 1e6, 3)
+            result["no_io"]["step_budget_us"] = NOIO_STEP_BUDGET_US
+            # ---- step 0 alone (the cold fill: about k misses per stream) ----
+            def cold_step(inst):
+                g = capture_steps(setup, inst, 1)
+                g.replay()
+                torch.cuda.synchronize()
+                best = None
+                for _ in range(3):
+                    setup.reset(inst)
+                    t0 = time.perf_counter()
+                    g.replay()
+                    torch.cuda.synchronize()
+                    dt = time.perf_counter() - t0
+                    best = dt if best is None else min(best, dt)
+                return best, int(setup.totals(inst)[0])
+            dt0_io, miss0 = cold_step(io)
+            dt0_noio, _ = cold_step(setup.noio)
+            b0 = miss0 * cfg.row_bytes
+            result["miss_fetch"]["cold_step"] = {
+                "bytes": b0, "misses": miss0, "us": round(dt0_io * 1e6, 1),
+                "us_no_io": round(dt0_noio * 1e6, 1),
+                "GBps": round(b0 / dt0_io / 1e9, 3),
+                "GBps_io_minus_noio": (round(b0 / (dt0_io - dt0_noio) / 1e9, 3)
+                                       if dt0_io > dt0_noio else None),
+                "mode": "step 0 alone from a cold cache, one HIP graph, best of 3"}
             if not args.no_probe:
                 lp = link_probe(torch, hb)
                 result["link_peak"] = lp
                 result["roofline"]["peak_measured"] = lp["measured_peak_GBps"]
                 result["roofline"]["frac_of_measured"] = round(fetch_gbps / lp["measured_peak_GBps"], 4)
+                cs = result["miss_fetch"]["cold_step"]
+                cs["frac_of_measured"] = round(cs["GBps"] / lp["measured_peak_GBps"], 4)
             if not args.no_cpu_baseline:
-                result["cpu_baseline"] = cpu_baseline(setup, K)
+                result["cpu_baseline"] = cpu_baseline(setup, K, no_io_seconds=3.0)
                 result["cpu_baseline_threads"] = cpu_baseline(
                     setup, K, threads=min(cfg.streams, len(os.sched_getaffinity(0))),
                     min_seconds=5.0)

@@ -36,8 +36,14 @@
 //   * values: P^T (hi and lo bf16 parts, so the products keep ~16 more bits
 //     than a plain bf16 P) goes to LDS next to the rows, and
 //     wave w accumulates O^T for output dims 128w .. 128w+127 over the 64 rows
-//     with v_mfma_f32_16x16x16_bf16: the waves own disjoint dims, so nothing
-//     is combined across waves but the softmax sums;
+//     with v_mfma_f32_16x16x32_bf16: the waves own disjoint dims, so nothing
+//     is combined across waves but the softmax sums.  The V^T operand (one
+//     output dim, eight consecutive rows per lane) comes from the row-major
+//     tile through gfx950's transposing LDS read, ds_read_b64_tr_b16: within
+//     each 16-lane group, element j of lane i's result is element i % 4 of
+//     the 8 bytes addressed by lane 4 j + i / 4, so lane 4 j + q points at
+//     row j, dims 4 q .. 4 q + 3 of the block and every lane receives four
+//     rows of its own dim;
 //   * each split writes its partial (max, sum, unnormalised output) to a
 //     workspace, and a second kernel (8 workgroups per request and head
 //     block, coalesced over the partials' register order) merges the splits.
@@ -53,14 +59,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKSteps = kMlaDqk / 32;  // 18 steps of 32 dims for the scores
 constexpr int kTile = 16 * kMlaWaves;   // 64 rows per tile
 constexpr int kKRowPitch = kMlaDqk + 8;  // bf16 per LDS row: 1168 B (16-byte aligned, and
                                          // 16 consecutive rows start on distinct bank quads)
+constexpr int kPPitch = kTile + 8;        // shorts per head in the P^T tile: 144 B, so the 16
+                                         // heads' 16-byte operand reads hit distinct banks
 constexpr size_t kMlaKbufBytes = sizeof(uint16_t) * kTile * kKRowPitch;     // 73 KiB
-constexpr size_t kMlaPBytes = 2 * sizeof(uint16_t) * kMlaHB * kTile;        // 4 KiB (hi, lo)
+constexpr size_t kMlaPBytes = 2 * sizeof(uint16_t) * kMlaHB * kPPitch;      // 4.5 KiB (hi, lo)
 constexpr size_t kMlaRedBytes = sizeof(float) * 2 * kMlaWaves * kMlaHB;     // 0.5 KiB
 constexpr int kDBlocks = kMlaDv / 16;                 // 32 blocks of 16 output dims
 constexpr int kWaveDB = kDBlocks / kMlaWaves;         // 8 blocks (128 dims) per wave
@@ -72,12 +82,18 @@ __device__ __forceinline__ short bf16_bits(__bf16 x) {
   return __builtin_bit_cast(short, x);
 }
 
+// Transposing LDS read of 4 x 16-bit values (ds_read_b64_tr_b16).
+__device__ __forceinline__ short4_t lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4*)(__attribute__((address_space(3))) void*)(p));
+}
+
 __global__ void __launch_bounds__(kMlaThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 mla_decode_kernel(MlaArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   __bf16* kt = reinterpret_cast<__bf16*>(smem);                       // [64 rows][pitch]
-  short* phi_t = reinterpret_cast<short*>(smem + kMlaKbufBytes);       // [16 heads][64]
-  short* plo_t = phi_t + kMlaHB * kTile;
+  short* phi_t = reinterpret_cast<short*>(smem + kMlaKbufBytes);       // [16 heads][kPPitch]
+  short* plo_t = phi_t + kMlaHB * kPPitch;
   float* red = reinterpret_cast<float*>(smem + kMlaKbufBytes + kMlaPBytes);
   float* red_m = red;                      // [waves][16] tile maxima
   float* red_l = red + kMlaWaves * kMlaHB;  // [waves][16] softmax sums
@@ -112,44 +128,53 @@ mla_decode_kernel(MlaArgs a) {
   // request: load j (0 .. 17) covers rows 8 (j & 1) + lane / 8, bytes
   // 128 (j >> 1) + 16 (lane % 8) .. +15 of each, i.e. 8 rows x 128 contiguous
   // bytes, and goes to the LDS copy of the tile; the MFMA operands are read
-  // from there.  row_slot(tile0, m): slot of the wave's row m, -1 when
-  // outside the split or padding.
-  auto row_slot = [&](int tile0, int m) {
+  // from there.  A lane needs three slot-map entries per tile: the rows of
+  // its two lines (m = lane / 8, 8 + lane / 8) and its MFMA row
+  // (m = lane % 16).  They are read one tile ahead, so that no dependent
+  // index load sits between a tile's rows and their use, and the loads are
+  // unconditional (clamped, in-bounds addresses; rows outside the split or
+  // padding are replaced by zeros when stored), so that the compiler's
+  // wait counts follow the software pipeline exactly.
+  const int m0 = lane >> 3, m1 = 8 + (lane >> 3), mv = lane & 15;
+  auto slot_raw = [&](int tile0, int m) {
+    const int r = min(tile0 + 16 * wave + m, n_tok - 1);
+    return slots[r / a.T];
+  };
+  auto slot_ok = [&](int raw, int tile0, int m) {  // -1: outside the split, or padding
     const int r = tile0 + 16 * wave + m;
-    if (tile0 >= r_end || r >= r_end) return -1;
-    const int sl = slots[r / a.T];
-    return (sl >= 0 && sl < a.slots_total) ? sl : -1;
+    return (r < r_end && raw >= 0 && raw < a.slots_total) ? raw : -1;
   };
   bf16x8 kf[kKSteps];
-  auto load_rows = [&](int tile0, int sl0, int sl1) {  // rows lane/8 and 8 + lane/8
+  bool ok0 = false, ok1 = false;  // the lines in kf belong to rows that are attended
+  auto load_rows = [&](int tile0, int sl0, int sl1) {
     const uint8_t* rp[2];
     const int sls[2] = {sl0, sl1};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int m = 8 * half + (lane >> 3);
-      const int r = tile0 + 16 * wave + m;
+      const int r = tile0 + 16 * wave + (half ? m1 : m0);
       rp[half] = cbase + (int64_t)(sls[half] >= 0 ? sls[half] : 0) * a.row_bytes +
                  (int64_t)(r % a.T) * (2 * kMlaDqk) + 16 * (lane & 7);
     }
+    ok0 = sl0 >= 0;
+    ok1 = sl1 >= 0;
 #pragma unroll
     for (int j = 0; j < kKSteps; ++j)
-      kf[j] = sls[j & 1] >= 0
-                  ? __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(rp[j & 1] + 128 * (j >> 1)))
-                  : zero8;
+      kf[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(rp[j & 1] + 128 * (j >> 1)));
   };
   auto store_rows = [&]() {  // the loaded lines into the wave's 16 rows of the tile
 #pragma unroll
     for (int j = 0; j < kKSteps; ++j) {
-      const int m = 8 * (j & 1) + (lane >> 3);
+      const int m = (j & 1) ? m1 : m0;
       *reinterpret_cast<bf16x8*>(kt + (16 * wave + m) * kKRowPitch + 64 * (j >> 1) + 8 * (lane & 7)) =
-          kf[j];
+          ((j & 1) ? ok1 : ok0) ? kf[j] : zero8;
     }
   };
 
   // the first tile's rows are requested with the queries; each later tile's
   // rows while the previous tile is finished (software pipeline)
-  load_rows(r_begin, row_slot(r_begin, lane >> 3), row_slot(r_begin, 8 + (lane >> 3)));
-  bool valid = row_slot(r_begin, lane & 15) >= 0;  // the MFMA row of this lane
+  int raw0 = slot_raw(r_begin, m0), raw1 = slot_raw(r_begin, m1), rawv = slot_raw(r_begin, mv);
+  load_rows(r_begin, slot_ok(raw0, r_begin, m0), slot_ok(raw1, r_begin, m1));
+  bool valid = slot_ok(rawv, r_begin, mv) >= 0;  // the MFMA row of this lane
   // B-operand fragments of Q^T: head h, dims 32 ks + 8 g .. +7
   bf16x8 qf[kKSteps];
   {
@@ -157,19 +182,33 @@ mla_decode_kernel(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qh + 32 * ks);
   }
+  raw0 = slot_raw(r_begin + kTile, m0);
+  raw1 = slot_raw(r_begin + kTile, m1);
+  rawv = slot_raw(r_begin + kTile, mv);
+  // Everything above has landed before the loop (s_waitcnt vmcnt(0)): the
+  // compiler then knows the query fragments are not pending, and does not
+  // make the score MFMAs wait for the next tile's loads.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   float m_run = -INFINITY, l_run = 0.f;  // m_run: the workgroup's; l_run: this wave's rows
   float4_t acc[kWaveDB];
 #pragma unroll
   for (int db = 0; db < kWaveDB; ++db) acc[db] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int tile0 = r_begin; tile0 < r_end; tile0 += kTile) {
-    const int sl0_next = row_slot(tile0 + kTile, lane >> 3);
-    const int sl1_next = row_slot(tile0 + kTile, 8 + (lane >> 3));
-    const bool valid_next = row_slot(tile0 + kTile, lane & 15) >= 0;
+    const int t1 = tile0 + kTile;
+    const int sl0_next = slot_ok(raw0, t1, m0);
+    const int sl1_next = slot_ok(raw1, t1, m1);
+    const bool valid_next = slot_ok(rawv, t1, mv) >= 0;
     const bool valid_now = valid;
     store_rows();
-    // the registers are free: request the next tile's rows
-    if (tile0 + kTile < r_end) load_rows(tile0 + kTile, sl0_next, sl1_next);
+    // the registers are free: request the next tile's rows, and the slot-map
+    // entries of the tile after it
+    if (t1 < r_end) {
+      load_rows(t1, sl0_next, sl1_next);
+      raw0 = slot_raw(t1 + kTile, m0);
+      raw1 = slot_raw(t1 + kTile, m1);
+      rawv = slot_raw(t1 + kTile, mv);
+    }
     valid = valid_next;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");  // the wave's rows in LDS
     __builtin_amdgcn_wave_barrier();
@@ -221,27 +260,32 @@ mla_decode_kernel(MlaArgs a) {
       phi[j] = bf16_bits(hi);
       plo[j] = bf16_bits(lo);
     }
-    *reinterpret_cast<short4_t*>(phi_t + h * kTile + 16 * wave + 4 * g) = phi;
-    *reinterpret_cast<short4_t*>(plo_t + h * kTile + 16 * wave + 4 * g) = plo;
+    *reinterpret_cast<short4_t*>(phi_t + h * kPPitch + 16 * wave + 4 * g) = phi;
+    *reinterpret_cast<short4_t*>(plo_t + h * kPPitch + 16 * wave + 4 * g) = plo;
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < kWaveDB; ++db) acc[db] *= alpha;
     }
     lds_barrier();  // B: P tile written
-    // O^T[128 wave + 16 db + 4g + j][h] += sum over the tile's 64 rows
-#pragma unroll 2
-    for (int rg = 0; rg < kMlaWaves; ++rg) {
-      const short4_t bh = *reinterpret_cast<const short4_t*>(phi_t + h * kTile + 16 * rg + 4 * g);
-      const short4_t bl = *reinterpret_cast<const short4_t*>(plo_t + h * kTile + 16 * rg + 4 * g);
+    // O^T[128 wave + 16 db + 4g + j][h] += sum over the tile's 64 rows, 32 at a
+    // time: this lane's k range is rows 32 rc + 8 g .. +7.  Its two transposing
+    // reads point at row 32 rc + 8 g + (lane & 15) / 4 (+ 4), dims
+    // 4 (lane & 3) .. +3 of the 16-dim block.
+    const __bf16* vrow = kt + (8 * g + ((lane & 15) >> 2)) * kKRowPitch + 4 * (lane & 3) +
+                         16 * kWaveDB * wave;
+#pragma unroll
+    for (int rc = 0; rc < kTile / 32; ++rc) {
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(phi_t + h * kPPitch + 32 * rc + 8 * g);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(plo_t + h * kPPitch + 32 * rc + 8 * g);
 #pragma unroll
       for (int db = 0; db < kWaveDB; ++db) {
-        short4_t va;  // A operand: V^T[d = 128 wave + 16 db + (lane & 15)][rows 4g .. 4g+3]
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          va[t] = bf16_bits(
-              kt[(16 * rg + 4 * g + t) * kKRowPitch + 16 * (kWaveDB * wave + db) + (lane & 15)]);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bh, acc[db], 0, 0, 0);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, bl, acc[db], 0, 0, 0);
+        const __bf16* vp = vrow + 32 * rc * kKRowPitch + 16 * db;
+        const short4_t v0 = lds_read_tr16(vp);
+        const short4_t v1 = lds_read_tr16(vp + 4 * kKRowPitch);
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, short8_t{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bh, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, bl, acc[db], 0, 0, 0);
       }
     }
     lds_barrier();  // C: the tile buffers are free for the next tile
