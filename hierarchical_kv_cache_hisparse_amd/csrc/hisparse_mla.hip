@@ -313,7 +313,14 @@ mla_decode_kernel(MlaArgs a) {
 // lse = m + log(sum).  The partials keep the split kernel's register order
 // (float4 (db, lane) = dims 16 db + 4 (lane >> 4) + 0..3 of head lane & 15), so
 // the reads here are fully coalesced.  grid = B * HBn * kMlaMergeParts,
-// 256 threads, one float4 of the 16 x 512 block per thread.
+// 256 threads, one float4 of the 16 x 512 block per thread.  With up to
+// kMergeRegSplits splits the thread's partials are requested at the start,
+// with the maxima and sums, so the weights are computed while they arrive
+// (one memory round trip instead of three), and the weights of the 16 heads
+// x S splits are computed by one thread each (shuffle reductions over a
+// head's 16-lane group) instead of one serial loop per head.
+constexpr int kMergeRegSplits = 16;
+
 __global__ void __launch_bounds__(256) mla_combine_kernel(MlaArgs a) {
   extern __shared__ float wsh[];  // [16 heads][S] weights, [16] 1/L, [16 heads][S] sums
   const int id = blockIdx.x;
@@ -323,14 +330,48 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaArgs a) {
   const int hb = bhb - b * a.HBn;
   const int pid0 = bhb * a.S;
   const int tid = threadIdx.x;
+  constexpr int kF4 = kMlaHB * kMlaDv / 4;  // 2048 float4 per split
+  static_assert(kF4 / kMlaMergeParts == 256, "one float4 per thread");
+  const int f = part_no * (kF4 / kMlaMergeParts) + tid;
+  const float4_t* pbase = reinterpret_cast<const float4_t*>(a.part + (int64_t)pid0 * kMlaHB * kMlaDv) + f;
+  const bool in_regs = a.S <= kMergeRegSplits;
+  float4_t pv[kMergeRegSplits];
+  if (in_regs) {
+#pragma unroll
+    for (int sp = 0; sp < kMergeRegSplits; ++sp)
+      if (sp < a.S) pv[sp] = pbase[(int64_t)sp * kF4];
+  }
   float* sums = wsh + kMlaHB * a.S + kMlaHB;
-  for (int x = tid; x < kMlaHB * a.S; x += 256) {
-    const int hh = x / a.S, sp = x - hh * a.S;
-    wsh[x] = a.part_ml[((int64_t)(pid0 + sp) * kMlaHB + hh) * 2];
-    sums[x] = a.part_ml[((int64_t)(pid0 + sp) * kMlaHB + hh) * 2 + 1];
+  if (in_regs) {
+    // thread (head tid / 16, split tid % 16): maximum and weighted sum over
+    // the head's splits with shuffles inside its 16-lane group
+    const int h2 = tid >> 4, sp2 = tid & 15;
+    float ms = -INFINITY, ls = 0.f;
+    if (sp2 < a.S) {
+      ms = a.part_ml[((int64_t)(pid0 + sp2) * kMlaHB + h2) * 2];
+      ls = a.part_ml[((int64_t)(pid0 + sp2) * kMlaHB + h2) * 2 + 1];
+    }
+    float m = ms;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float w = (ms == -INFINITY) ? 0.f : expf(ms - m);
+    float L = w * ls;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) L += __shfl_xor(L, o);
+    if (sp2 < a.S) wsh[h2 * a.S + sp2] = w;
+    if (sp2 == 0) {
+      wsh[kMlaHB * a.S + h2] = L > 0.f ? 1.f / L : 0.f;
+      if (part_no == 0) a.lse[(int64_t)b * a.H + hb * kMlaHB + h2] = L > 0.f ? m + logf(L) : -INFINITY;
+    }
+  } else {
+    for (int x = tid; x < kMlaHB * a.S; x += 256) {
+      const int hh = x / a.S, sp = x - hh * a.S;
+      wsh[x] = a.part_ml[((int64_t)(pid0 + sp) * kMlaHB + hh) * 2];
+      sums[x] = a.part_ml[((int64_t)(pid0 + sp) * kMlaHB + hh) * 2 + 1];
+    }
   }
   __syncthreads();
-  if (tid < kMlaHB) {
+  if (!in_regs && tid < kMlaHB) {
     float m = -INFINITY;
     for (int sp = 0; sp < a.S; ++sp) m = fmaxf(m, wsh[tid * a.S + sp]);
     float L = 0.f;
@@ -344,19 +385,18 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(MlaArgs a) {
     if (part_no == 0) a.lse[(int64_t)b * a.H + hb * kMlaHB + tid] = L > 0.f ? m + logf(L) : -INFINITY;
   }
   __syncthreads();
-  constexpr int kF4 = kMlaHB * kMlaDv / 4;  // 2048 float4 per split
-  for (int f = part_no * (kF4 / kMlaMergeParts) + tid; f < (part_no + 1) * (kF4 / kMlaMergeParts);
-       f += 256) {
-    const int lane = f & 63, db = f >> 6;
-    const int hh = lane & 15, g = lane >> 4;
-    float4_t o = {0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < a.S; ++sp)
-      o += wsh[hh * a.S + sp] *
-           reinterpret_cast<const float4_t*>(a.part + (int64_t)(pid0 + sp) * kMlaHB * kMlaDv)[f];
-    o *= wsh[kMlaHB * a.S + hh];
-    *reinterpret_cast<float4_t*>(a.out + ((int64_t)b * a.H + hb * kMlaHB + hh) * kMlaDv + 16 * db +
-                                 4 * g) = o;
+  const int lane = f & 63, db = f >> 6;
+  const int hh = lane & 15, g = lane >> 4;
+  float4_t o = {0.f, 0.f, 0.f, 0.f};
+  if (in_regs) {
+#pragma unroll
+    for (int sp = 0; sp < kMergeRegSplits; ++sp)
+      if (sp < a.S) o += wsh[hh * a.S + sp] * pv[sp];
+  } else {
+    for (int sp = 0; sp < a.S; ++sp) o += wsh[hh * a.S + sp] * pbase[(int64_t)sp * kF4];
   }
+  o *= wsh[kMlaHB * a.S + hh];
+  *reinterpret_cast<float4_t*>(a.out + ((int64_t)b * a.H + hb * kMlaHB + hh) * kMlaDv + 16 * db + 4 * g) = o;
 }
 
 }  // namespace
