@@ -1,0 +1,79 @@
+"""Host-side checks of the benchmark script (no GPU): it refuses more than
+one GPU, the committed counter summaries it reads are current and
+self-consistent, its rocprofv3 summary writer round-trips counters through
+the same parser, and its CPU baseline runs the oracle on a small trace."""
+import os
+import subprocess
+import sys
+import types
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("kernel,mode", [("resolve_kernel", "fused"), ("resolve_kernel", "noio"),
+                                         ("fetch_kernel", "split")])
+def test_committed_traffic_is_current(kernel, mode):
+    """The PMC summaries behind the bench's traffic figures were taken on the
+    kernel sources in the tree (else the bench reports no traffic), and the
+    scaled byte counts are of the size the workload implies."""
+    t = bench.committed_traffic(kernel, "tokens_b8_L128k", mode)
+    assert t is not None, "PMC summaries missing or taken on other kernel sources"
+    # per launch: 8 streams x 2048 selections of metadata at least; with the
+    # copies, about 2.7 MB of miss rows read and written on average
+    assert t["FETCH_SIZE"] > 8 * 2048 * 4 and t["WRITE_SIZE"] > 8 * 2048 * 4
+    if mode != "noio":
+        assert 2.0e6 < t["FETCH_SIZE"] < 2.0e7
+        assert 2.0e6 < t["WRITE_SIZE"] < 2.0e7
+
+
+def test_summary_writer_round_trip(tmp_path, monkeypatch):
+    """A synthetic rocprofv3 counter CSV -> the Markdown summary -> the parser
+    the bench uses: the calibration copy's reading scales the kernel's."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    d = tmp_path / "raw" / "node"
+    d.mkdir(parents=True)
+    rows = ["Kernel_Name,Counter_Name,Counter_Value"]
+    rows += ["hsp::resolve_kernel<4>(args),FETCH_SIZE,100.0",
+             "hsp::resolve_kernel<4>(args),FETCH_SIZE,300.0",
+             "hsp::probe_host_read_kernel(args),FETCH_SIZE,131072.0"]
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_rocprof(str(tmp_path / "raw"), "pmc_fetch_size_x_fused", "cmd")
+    rows[1:] = [r.replace("FETCH_SIZE", "WRITE_SIZE") for r in rows[1:]]
+    rows[-1] = "hsp::probe_host_read_kernel(args),WRITE_SIZE,262144.0"
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_rocprof(str(tmp_path / "raw"), "pmc_write_size_x_fused", "cmd")
+    t = bench.committed_traffic("resolve_kernel", "x", "fused")
+    # mean 200 KiB per dispatch; the 256 MiB copy read as 128 MiB -> x2, written as 256 MiB -> x1
+    assert t["FETCH_SIZE"] == pytest.approx(200 * 1024 * 2.0)
+    assert t["WRITE_SIZE"] == pytest.approx(200 * 1024 * 1.0)
+    text = (tmp_path / "profiles" / "pmc_fetch_size_x_fused.md").read_text()
+    assert "Command: `cmd`" in text and "| resolve_kernel | FETCH_SIZE | 2 | 200.0 | 400.0 |" in text
+
+
+def test_cpu_baseline_runs_the_oracle():
+    from tests.harness import fill_host, make_trace
+    from workload import WORKLOADS
+    cfg = WORKLOADS[2].scaled(B=2, L0=6000, C=1200, R=16, k=600, steps=3)
+    trace = make_trace(cfg)
+    hosts = {(b, l): (None, np.zeros((cfg.l_cap, cfg.row_bytes), np.uint8))
+             for b in range(cfg.B) for l in range(cfg.layers)}
+    fill_host(cfg, lambda b, l: hosts[(b, l)][1], trace, list(hosts))
+    setup = types.SimpleNamespace(cfg=cfg, trace=trace, hosts=hosts, queries=1)
+    r = bench.cpu_baseline(setup, cfg.steps, threads=2, min_seconds=0.2, no_io_seconds=0.1)
+    assert r["kind"] == "oracle" and r["cores"] == 2 and r["unit"] == "entries/s"
+    assert r["value"] > 0 and r["no_io_value"] > 0
+    assert "trace of all 2 streams" in r["sample"]
