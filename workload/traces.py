@@ -65,10 +65,18 @@ def _draw_distinct(rng, sampler, n: int, taken: np.ndarray) -> np.ndarray:
     Draws are examined in the order they were made; the first occurrence of a
     new position is accepted, later repeats and already-taken positions are
     rejected and replaced by further draws.  Accepted positions are marked.
+    Raises ValueError when the distribution leaves too few free positions to
+    finish in a bounded number of rounds (a context barely larger than the
+    selection, under a distribution concentrated on its taken end).
     """
     out = []
     need = n
+    rounds = 0
     while need > 0:
+        rounds += 1
+        if rounds > 20000:
+            raise ValueError(f"could not draw {n} distinct free positions ({need} missing): "
+                             "the context is too small for this distribution")
         cand = sampler(max(2 * need, 16))
         _, first = np.unique(cand, return_index=True)
         first.sort()
