@@ -214,18 +214,49 @@ def link_probe(torch, hb):
 PROFILES = os.path.join(ROOT, "profiles")
 # the resolve and fetch kernels' sources: PMC summaries taken on other sources
 # are not used for the traffic figure
-KERNEL_SOURCES = [os.path.join(ROOT, "hierarchical_kv_cache_hisparse_amd", "csrc", f)
-                  for f in ("hisparse_kernels.hip", "hisparse_device.h", "hisparse_internal.h")]
+CSRC = os.path.join(ROOT, "hierarchical_kv_cache_hisparse_amd", "csrc")
+# the sources each kernel family is built from; a counter summary is used only
+# while the hash of its family's sources matches the one it recorded
+SOURCE_FAMILIES = {
+    "resolve": ("hisparse_kernels.hip", "hisparse_device.h", "hisparse_internal.h"),
+    "mla": ("hisparse_mla.hip", "hisparse_device.h", "hisparse_internal.h"),
+    "topk": ("hisparse_topk.hip", "hisparse_device.h", "hisparse_internal.h"),
+}
+SHA_LINE = {"resolve": "Kernel source sha256[:16]", "mla": "MLA kernel source sha256[:16]",
+            "topk": "Top-k kernel source sha256[:16]"}
 CALIBRATION_BYTES = 256 << 20
 
 
-def kernel_source_sha():
+def kernel_source_sha(family="resolve"):
     import hashlib
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
+    for name in SOURCE_FAMILIES[family]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_family(kernel):
+    if kernel.startswith("mla_"):
+        return "mla"
+    if kernel.startswith("topk_"):
+        return "topk"
+    return "resolve"
+
+
+def calibration_copy():
+    """The known-size device copy (256 MiB with 16-byte loads) whose counter
+    readings scale FETCH_SIZE and WRITE_SIZE in the PMC runs."""
+    import torch
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    torch.cuda.synchronize()
+    hb.hisparse_probe_host_read(torch.cuda.current_stream().cuda_stream, src.data_ptr(),
+                                dst.data_ptr(), CALIBRATION_BYTES, 1024)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def short_kernel_name(name):
@@ -243,8 +274,8 @@ def summarize_rocprof(directory, label, command):
     into a short Markdown summary under profiles/."""
     import csv
     import glob
-    lines = [f"# {label}", "", f"Command: `{command}`", "",
-             f"Kernel source sha256[:16]: {kernel_source_sha()}", ""]
+    lines = [f"# {label}", "", f"Command: `{command}`", ""]
+    lines += [f"{SHA_LINE[fam]}: {kernel_source_sha(fam)}" for fam in SOURCE_FAMILIES] + [""]
     stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
     trace = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
     pmc = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
@@ -294,29 +325,39 @@ def summarize_rocprof(directory, label, command):
     print(out)
 
 
-def committed_traffic(kernel, label, mode):
-    """HBM+link bytes per launch of `kernel` from the committed PMC summaries
-    (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, each scaled by the counter's
-    reading for a device copy of known size), or None when absent or taken on
-    a different kernel source."""
+def committed_traffic(kernels, label, mode):
+    """HBM+link bytes per call from the committed PMC summaries: FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch) of each kernel in `kernels` (one name,
+    or several launched once per call, summed), each scaled by the counter's
+    reading for a device copy of known size.  None when a summary is absent
+    or was taken on other sources of the kernels' family."""
     import re
+    kernels = (kernels,) if isinstance(kernels, str) else tuple(kernels)
+    fam = kernel_family(kernels[0])
     vals = {}
-    sha = kernel_source_sha()
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         path = os.path.join(PROFILES, f"pmc_{counter.lower()}_{label}_{mode}.md")
         if not os.path.exists(path):
             return None
         text = open(path).read()
-        if f"Kernel source sha256[:16]: {sha}" not in text:
+        rec = re.search(r"^" + re.escape(SHA_LINE[fam]) + r": (\w+)$", text, re.M)
+        if not rec or rec.group(1) != kernel_source_sha(fam):
             return None
         got = {}
         for m in re.finditer(r"pmc: kernel=(\S+) counter=(\S+) mean=([0-9.eE+-]+)", text):
             got[m.group(1)] = float(m.group(3))
-        if kernel not in got or "probe_host_read_kernel" not in got:
+        if any(k not in got for k in kernels) or "probe_host_read_kernel" not in got:
             return None
         scale = (CALIBRATION_BYTES / 1024.0) / got["probe_host_read_kernel"]
-        vals[counter] = got[kernel] * scale * 1024.0
+        vals[counter] = sum(got[k] for k in kernels) * scale * 1024.0
     return vals
+
+
+def traffic_fields(t):
+    """The roofline's traffic entries from committed_traffic's result."""
+    return {"traffic": round(t["FETCH_SIZE"] + t["WRITE_SIZE"]) if t else None,
+            "traffic_read_bytes": round(t["FETCH_SIZE"]) if t else None,
+            "traffic_write_bytes": round(t["WRITE_SIZE"]) if t else None}
 
 
 def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
@@ -465,9 +506,12 @@ def mla_study(setup, K, H):
     return {"metric": "sparse MLA decode attention over the slot map", "value": round(us, 3),
             "unit": "us per layer call", "higher_is_better": False, "workload": cfg.name,
             "requests": cfg.B, "heads": H, "attended_rows_per_request": n_tok,
-            "roofline": {"bound": "hbm", "achieved": round(byts / us / 1e3, 1), "peak": HBM_PEAK_GBPS,
+            "roofline": {"bound": "hbm", "kernel": "mla_decode_kernel + mla_combine_kernel",
+                         "achieved": round(byts / us / 1e3, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(byts / us / 1e3 / HBM_PEAK_GBPS, 4),
-                         "per_launch_bytes": byts},
+                         "per_launch_bytes": byts,
+                         **traffic_fields(committed_traffic(
+                             ("mla_decode_kernel", "mla_combine_kernel"), f"{cfg.label}_h{H}", "mla"))},
             "mfma": {"achieved_TFLOPs": round(flops / us / 1e6, 2), "peak_TFLOPs": 2500.0,
                      "frac": round(flops / us / 1e6 / 2500.0, 5)},
             "timing": "torch events around each launch, median of steps 1..",
@@ -556,11 +600,16 @@ def topk_study(cfg, K, W):
             "rows": B, "positions_per_row": N, "k": k,
             "scores_per_s": round(B * N / us * 1e6, 1),
             "graph_us_per_call": round(graph_us, 3),
-            "roofline": {"bound": "hbm", "achieved": round(byts / us / 1e3, 1),
+            "roofline": {"bound": "hbm",
+                         "kernel": "topk_hist_kernel + topk_filter_kernel + topk_finish_kernel",
+                         "achieved": round(byts / us / 1e3, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(byts / us / 1e3 / HBM_PEAK_GBPS, 4),
                          "per_launch_bytes": byts,
-                         "achieved_graph": round(byts / graph_us / 1e3, 1)},
+                         "achieved_graph": round(byts / graph_us / 1e3, 1),
+                         **traffic_fields(committed_traffic(
+                             ("topk_hist_kernel", "topk_filter_kernel", "topk_finish_kernel"),
+                             cfg.label, "topk"))},
             "timing": "torch events around the three launches, median of K calls",
             "cpu_baseline": {"value": round(t_cpu / n_cpu * B * 1e6, 1), "unit": "us per layer call",
                              "cores": 1, "kind": "oracle",
@@ -744,7 +793,10 @@ def main():
     if args.steps is None:
         args.steps = base.steps
     if args.topk:
-        print(json.dumps(topk_study(base, max(1, args.steps), args.warmup)), flush=True)
+        result = topk_study(base, max(1, args.steps), args.warmup)
+        if args.calibration_copy:
+            calibration_copy()
+        print(json.dumps(result), flush=True)
         return
     S = max(args.steps, args.warmup, 1)
     Q = max(1, args.queries)
@@ -763,7 +815,10 @@ def main():
         return
     if args.mla_attention:
         try:
-            print(json.dumps(mla_study(setup, K, args.heads)), flush=True)
+            result = mla_study(setup, K, args.heads)
+            if args.calibration_copy:
+                calibration_copy()
+            print(json.dumps(result), flush=True)
         finally:
             setup.close()
         return
@@ -824,14 +879,7 @@ def main():
         value = entries / elapsed
 
         if args.calibration_copy:
-            src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda:0")
-            dst = torch.empty_like(src)
-            src.fill_(3)
-            torch.cuda.synchronize()
-            hb.hisparse_probe_host_read(torch.cuda.current_stream().cuda_stream, src.data_ptr(),
-                                        dst.data_ptr(), CALIBRATION_BYTES, 1024)
-            torch.cuda.synchronize()
-            del src, dst
+            calibration_copy()
 
         fused = timing["fetch_launches"] == 0
         resolve_avg_s = timing["resolve_ms"] / max(1, timing["resolve_launches"]) / 1e3

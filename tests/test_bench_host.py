@@ -40,6 +40,23 @@ def test_committed_traffic_is_current(kernel, mode):
         assert 2.0e6 < t["WRITE_SIZE"] < 2.0e7
 
 
+def test_committed_traffic_of_attention_and_topk():
+    """The attention and top-k counter summaries are current for their own
+    kernel sources: attention reads every attended row about once (16 x 2048
+    rows of 1152 B) plus the split partials; top-k reads the 16 x 131072
+    scores twice (histogram, filter)."""
+    rows = 16 * 2048 * 1152
+    m = bench.committed_traffic(("mla_decode_kernel", "mla_combine_kernel"),
+                                "tokens_b16x8_L256k_h16", "mla")
+    assert m is not None
+    assert rows < m["FETCH_SIZE"] < 1.6 * rows
+    scores = 16 * 131072 * 4
+    t = bench.committed_traffic(("topk_hist_kernel", "topk_filter_kernel", "topk_finish_kernel"),
+                                "tokens_b16x8_L128k", "topk")
+    assert t is not None
+    assert 2 * scores < t["FETCH_SIZE"] < 3 * scores
+
+
 def test_summary_writer_round_trip(tmp_path, monkeypatch):
     """A synthetic rocprofv3 counter CSV -> the Markdown summary -> the parser
     the bench uses: the calibration copy's reading scales the kernel's."""
