@@ -227,12 +227,21 @@ SHA_LINE = {"resolve": "Kernel source sha256[:16]", "mla": "MLA kernel source sh
 CALIBRATION_BYTES = 256 << 20
 
 
+def _code_only(text):
+    """Source text without comments and blank lines: edits to comments leave
+    the recorded hash (and the counters taken on that code) valid."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_sha(family="resolve"):
     import hashlib
     h = hashlib.sha256()
     for name in SOURCE_FAMILIES[family]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

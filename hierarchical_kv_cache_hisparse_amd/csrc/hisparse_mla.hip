@@ -18,8 +18,8 @@
 //   lse[h]      = log sum_i exp(score[h, i])
 //
 // CDNA4 mapping:
-//   * grid = (requests x head blocks of 16) x splits of the token rows, about
-//     two workgroups per CU (71 KiB of LDS each, so one computes while the
+//   * grid = (requests x head blocks of 16) x splits of the token rows, up to
+//     two workgroups per CU (78 KiB of LDS each, so one computes while the
 //     other waits for its rows); a workgroup (4 waves) walks its split in
 //     tiles of 64 rows, each row read once from HBM (16-byte loads, all in
 //     flight, the next tile's requested while the current one is finished);
