@@ -144,6 +144,12 @@ class Setup:
         hb, cfg = self.hb, self.cfg
         st = self.torch.cuda.current_stream().cuda_stream if stream is None else stream
         for l in range(cfg.layers):
+            if cfg.growth and s > 0 and self.queries == 1:
+                # the decode step of a growing context: append + resolve, one call
+                hb.hisparse_append_resolve(inst.h, st, l, self.rows[s, l].data_ptr(),
+                                           self.pos[s].data_ptr(), self.sel[s, l].data_ptr(),
+                                           self.ctx[s].data_ptr(), self.out[l].data_ptr())
+                continue
             if cfg.growth and s > 0:
                 hb.hisparse_append(inst.h, st, l, self.rows[s, l].data_ptr(), self.pos[s].data_ptr())
             if self.queries > 1:
@@ -684,14 +690,17 @@ def pipeline_study(setup, K, H):
                 st = torch.cuda.current_stream().cuda_stream
                 for s in range(K):
                     for l in range(L):
-                        if cfg.growth and s > 0:
-                            hb.hisparse_append(inst.h, st, l, setup.rows[s, l].data_ptr(),
-                                               setup.pos[s].data_ptr())
                         hb.hisparse_topk(st, scores[s * L + l].data_ptr(), stride, B,
                                          cfg.l_cap, setup.ctx[s].data_ptr(), k, tk_ws.data_ptr(),
                                          sel[l].data_ptr())
-                        hb.hisparse_resolve(inst.h, st, sel[l].data_ptr(), setup.ctx[s].data_ptr(),
-                                            l, setup.out[l].data_ptr())
+                        if cfg.growth and s > 0:
+                            hb.hisparse_append_resolve(inst.h, st, l, setup.rows[s, l].data_ptr(),
+                                                       setup.pos[s].data_ptr(), sel[l].data_ptr(),
+                                                       setup.ctx[s].data_ptr(),
+                                                       setup.out[l].data_ptr())
+                        else:
+                            hb.hisparse_resolve(inst.h, st, sel[l].data_ptr(),
+                                                setup.ctx[s].data_ptr(), l, setup.out[l].data_ptr())
                         hb.hisparse_sparse_mla_decode(inst.h, st, l, q.data_ptr(),
                                                       setup.out[l].data_ptr(), H, scale,
                                                       ws.data_ptr(), att.data_ptr(), lse.data_ptr())
@@ -1006,7 +1015,10 @@ def main():
                                       "mode": "one HIP graph of all steps, best of 3"}
             result["no_io"] = {"us_per_layer_call": round(per_call_us, 3),
                                "resolve_kernel_us": round(noio_kernel_us, 3),
-                               "includes_append_launch": bool(cfg.growth),
+                               "includes_append": bool(cfg.growth),
+                               "append": ("fused into the resolve launch (hisparse_append_resolve)"
+                                          if cfg.growth and Q == 1 and cfg.R > 0 else
+                                          "separate launch" if cfg.growth else None),
                                "target_us": budget_us,
                                "frac_of_decode_step_budget": round(
                                    per_call_us / (DECODE_STEP_BUDGET_US / BUDGET_LAYERS), 5),

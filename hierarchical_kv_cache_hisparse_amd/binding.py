@@ -105,6 +105,7 @@ def library():
             "hisparse_prefetch": [P, P, P, P, P, I32],
             "hisparse_load_window": [P, P, I32, P],
             "hisparse_append": [P, P, I32, P, P],
+            "hisparse_append_resolve": [P, P, I32, P, P, P, P, P],
             "hisparse_reset": [P, P, I32, I32],
             "hisparse_get_status": [P, P, ctypes.c_int],
             "hisparse_set_timing": [P, ctypes.c_int],
@@ -200,6 +201,12 @@ def hisparse_load_window(h, stream: int, layer: int, ctx_len: int) -> None:
 
 def hisparse_append(h, stream: int, layer: int, rows: int, pos: int) -> None:
     _check(library().hisparse_append(h, stream, layer, rows, pos), "hisparse_append")
+
+
+def hisparse_append_resolve(h, stream: int, layer: int, rows: int, pos: int, sel: int,
+                            ctx_len: int, out_slot: int) -> None:
+    _check(library().hisparse_append_resolve(h, stream, layer, rows, pos, sel, ctx_len, out_slot),
+           "hisparse_append_resolve")
 
 
 def hisparse_reset(h, stream: int, layer: int = -1, request: int = -1) -> None:

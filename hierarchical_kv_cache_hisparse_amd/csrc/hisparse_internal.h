@@ -93,7 +93,8 @@ hipError_t launch_init(const StreamView& v, hipStream_t s, int layer, int reques
                        bool clear_status);
 hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const int32_t* sel,
                           const int32_t* ctx_len, int32_t* out, int32_t* sel_copy,
-                          int multi_entries = 0);
+                          int multi_entries = 0, const uint8_t* app_rows = nullptr,
+                          const int32_t* app_pos = nullptr);
 hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid_x);
 hipError_t launch_prefetch_join(const StreamView& v, hipStream_t s, const int32_t* sel,
                                 const int32_t* sel_copy, const int32_t* pf_out, int32_t* out);

@@ -141,8 +141,17 @@ __device__ __forceinline__ bool test_bit(const uint32_t* bm, int s) {
 // Barriers (LDS only): Z after clearing LDS; 1 after classification (hit
 // bitmap, class counters, miss counts, error bits); 2 after the misses are
 // staged and the unreferenced slots counted; 3 after the victims are taken.
-// No global write happens before barrier 1, so a rejected row leaves the
-// stream untouched.
+// No write to the stream's state happens before barrier 1, so a rejected
+// row leaves the stream untouched.
+//
+// Fused append (`app_rows` not NULL; the host calls it only with a resident
+// window, R >= 1): before resolving, the request's new row goes to host
+// history row pos = app_pos[b] and to ring slot C + pos mod R, as the
+// separate append does.  Nothing in the resolution reads either: pos is the
+// last position of the context, hence resident (never looked up, never
+// fetched), and misses are fetched into LRU slots only; so the stores run
+// alongside the resolution and the launch's end orders them before any later
+// reader.
 //
 // Several query tokens per request (`ke` > 0): the row holds ke entries (the
 // queries' selections one after another) and may repeat positions.  The step
@@ -153,11 +162,12 @@ __device__ __forceinline__ bool test_bit(const uint32_t* bm, int s) {
 // the union written in first-occurrence order.  The first entries leave
 // their slot in LDS, and after barrier 3 every repeat is served that slot.
 // ---------------------------------------------------------------------------
-template <int IPT>
+template <int IPT, bool kAppend>
 __global__ void __launch_bounds__(kMaxThreads)
     resolve_kernel(StreamView v, int layer, const int32_t* __restrict__ sel_all,
                    const int32_t* __restrict__ ctx_len, int32_t* __restrict__ out_all,
-                   int32_t* __restrict__ sel_copy, int ke_multi) {
+                   int32_t* __restrict__ sel_copy, int ke_multi,
+                   const uint8_t* __restrict__ app_rows, const int32_t* __restrict__ app_pos) {
   extern __shared__ int lds[];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -191,6 +201,26 @@ __global__ void __launch_bounds__(kMaxThreads)
   int* hash = misc + 8;
   int* first = hash + (multi ? H : 0);
   int* eslot = hash;
+
+  // ---- fused append (see above): host row and ring slot of the new position
+  // (a separate instantiation, so that the plain resolve carries none of it)
+  if (kAppend && R > 0) {
+    const int32_t pos = app_pos[b];
+    if (pos >= v.l_cap) {
+      if (tid == 0) atomicOr(status_word(v), HISPARSE_STATUS_CTX_RANGE);
+    } else if (pos >= 0) {
+      const int cpr = v.row_bytes >> 4;
+      const u32x4* src = reinterpret_cast<const u32x4*>(app_rows + (int64_t)b * v.row_bytes);
+      u32x4* hrow = reinterpret_cast<u32x4*>(v.host[layer * v.B + b] + (int64_t)pos * v.row_bytes);
+      u32x4* ring = reinterpret_cast<u32x4*>(
+          v.cache + ((int64_t)(layer * v.B + b) * (C + R) + C + pos % R) * v.row_bytes);
+      for (int c = tid; c < cpr; c += BD) {
+        const u32x4 val = src[c];
+        hrow[c] = val;
+        ring[c] = val;
+      }
+    }
+  }
 
   // ---- Phase A: independent loads; clear LDS ------------------------------
   int32_t p[IPT], o[IPT], q2[IPT], slot[IPT];
@@ -695,15 +725,19 @@ ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries)
 
 hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const int32_t* sel,
                           const int32_t* ctx_len, int32_t* out, int32_t* sel_copy,
-                          int multi_entries) {
+                          int multi_entries, const uint8_t* app_rows, const int32_t* app_pos) {
   const ResolveShape sh =
       resolve_shape(v.k, v.C, (v.flags & HISPARSE_DEBUG_VALIDATE) != 0, multi_entries);
   const dim3 grid(v.B), block(sh.threads);
   switch (sh.items) {
 #define HSP_RESOLVE_CASE(N)                                                                     \
   case N:                                                                                       \
-    hipLaunchKernelGGL(resolve_kernel<N>, grid, block, sh.lds_bytes, s, v, layer, sel, ctx_len, \
-                       out, sel_copy, multi_entries);                                           \
+    if (app_rows)                                                                               \
+      hipLaunchKernelGGL((resolve_kernel<N, true>), grid, block, sh.lds_bytes, s, v, layer, sel,  \
+                         ctx_len, out, sel_copy, multi_entries, app_rows, app_pos);             \
+    else                                                                                        \
+      hipLaunchKernelGGL((resolve_kernel<N, false>), grid, block, sh.lds_bytes, s, v, layer, sel, \
+                         ctx_len, out, sel_copy, multi_entries, app_rows, app_pos);             \
     break;
     HSP_RESOLVE_CASE(1)
     HSP_RESOLVE_CASE(2)

@@ -148,7 +148,8 @@ bool capturing(hipStream_t s) {
 
 // resolve kernel (+ fetch unless NO_IO) of one layer on one stream
 int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_t* ctx_len,
-                    int layer, int32_t* out, int32_t* sel_copy, int multi_entries = 0) {
+                    int layer, int32_t* out, int32_t* sel_copy, int multi_entries = 0,
+                    const uint8_t* app_rows = nullptr, const int32_t* app_pos = nullptr) {
   const bool io = !(h->cfg.flags & HISPARSE_NO_IO);
   TimedCall* tc = nullptr;
   if (h->timing && !capturing(s)) {
@@ -160,7 +161,8 @@ int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_
     tc->fetched = io && !h->view.fuse_fetch;
     HIP_TRY(hipEventRecord(tc->e0, s));
   }
-  HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy, multi_entries));
+  HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy, multi_entries, app_rows,
+                         app_pos));
   if (tc) HIP_TRY(hipEventRecord(tc->e1, s));
   if (io && !h->view.fuse_fetch) {
     HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
@@ -439,6 +441,25 @@ int hisparse_append(hisparse_t h, hipStream_t stream, int32_t layer, const void*
     return fail(HISPARSE_ERR_INVALID_ARG, "rows must be 16-byte aligned");
   HIP_TRY(launch_append(h->view, stream, layer, static_cast<const uint8_t*>(rows), pos));
   return HISPARSE_OK;
+}
+
+int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, const void* rows,
+                            const int32_t* pos, const int32_t* sel, const int32_t* ctx_len,
+                            int32_t* out_slot) {
+  if (!h || !rows || !pos || !sel || !ctx_len || !out_slot)
+    return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (reinterpret_cast<uintptr_t>(rows) % 16 != 0)
+    return fail(HISPARSE_ERR_INVALID_ARG, "rows must be 16-byte aligned");
+  if (h->cfg.resident_window == 0 || h->pending[layer]) {
+    // the appended position may be fetched by this resolve (no window), or the
+    // layer was resolved early: the append goes first, in its own launch
+    HIP_TRY(launch_append(h->view, stream, layer, static_cast<const uint8_t*>(rows), pos));
+    return hisparse_resolve(h, stream, sel, ctx_len, layer, out_slot);
+  }
+  return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr, 0,
+                         static_cast<const uint8_t*>(rows), pos);
 }
 
 int hisparse_reset(hisparse_t h, hipStream_t stream, int32_t layer, int32_t request) {

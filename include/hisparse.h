@@ -45,8 +45,8 @@
  * (hisparse_get_status): that stream's state is left untouched and its
  * out_slot row is all -1.
  *
- * Asynchrony.  hisparse_resolve, hisparse_prefetch, hisparse_append,
- * hisparse_load_window and hisparse_reset only enqueue work on the given
+ * Asynchrony.  hisparse_resolve, hisparse_append_resolve, hisparse_prefetch,
+ * hisparse_append, hisparse_load_window and hisparse_reset only enqueue work on the given
  * stream(s): they never synchronize, allocate or read device memory on the
  * host, so they can be captured into a HIP graph (prefetch forks and joins
  * by events, which capture as graph edges).  A handle is not thread-safe.
@@ -247,6 +247,20 @@ int hisparse_load_window(hisparse_t h, hipStream_t stream, int32_t layer,
  * context grows in host memory.]  Errors: INVALID_ARG, HIP. */
 int hisparse_append(hisparse_t h, hipStream_t stream, int32_t layer, const void* rows,
                     const int32_t* pos);
+
+/* hisparse_append followed by hisparse_resolve on the same layer, in one
+ * launch: the decode step of a growing context, where each layer's new row
+ * is appended and its selections resolved [P2 Timeline].  Arguments as for
+ * the two calls (ctx_len = pos + 1 for every appending request); results
+ * are identical to calling them in order on `stream`.  With a resident
+ * window (R >= 1) the appended position is resident, so the resolution
+ * neither looks it up nor fetches it and the row stores run inside the
+ * resolve launch; without a window, or when `layer` has a pending prefetch,
+ * the two calls are made as separate launches.  Graph-capturable like
+ * hisparse_resolve.  Errors: INVALID_ARG, HIP. */
+int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, const void* rows,
+                            const int32_t* pos, const int32_t* sel, const int32_t* ctx_len,
+                            int32_t* out_slot);
 
 /* Return streams to the empty state (every slot free, clock 0).  layer and
  * request select one stream; -1 means all.  Used for admission and reuse of

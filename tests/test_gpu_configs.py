@@ -62,11 +62,11 @@ def test_full_size_pages_no_io():
     _run_full(5, flags=hb.HISPARSE_NO_IO)
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3])
-def test_full_size_graph_of_all_steps(cfg_id):
-    """All steps (and, for the growing workload, the appends) captured as one
-    HIP graph on a side stream and replayed once from a cold cache, as the
-    benchmark times them.  The slot map buffer is rewritten by every step, so
+@pytest.mark.parametrize("cfg_id,fused_append", [(2, False), (3, False), (3, True)])
+def test_full_size_graph_of_all_steps(cfg_id, fused_append):
+    """All steps (and, for the growing workload, the appends: separate calls,
+    or fused into the resolve calls) captured as one HIP graph on a side
+    stream and replayed once from a cold cache, as the benchmark times them.  The slot map buffer is rewritten by every step, so
     the last step's map is compared; the LRU state, eviction log, counters,
     running totals and slot bytes of the sampled streams after the last step
     must equal the oracle's after all steps."""
@@ -93,6 +93,12 @@ def test_full_size_graph_of_all_steps(cfg_id):
                 st = torch.cuda.current_stream().cuda_stream
                 for s in range(cfg.steps):
                     for l in range(cfg.layers):
+                        if cfg.growth and s > 0 and fused_append:
+                            hb.hisparse_append_resolve(
+                                run.gpu.h, st, l, rows[s, l].data_ptr(), run.pos_dev[s].data_ptr(),
+                                run.sel_dev[s, l].data_ptr(), run.ctx_dev[s].data_ptr(),
+                                run.out_dev[l].data_ptr())
+                            continue
                         if cfg.growth and s > 0:
                             hb.hisparse_append(run.gpu.h, st, l, rows[s, l].data_ptr(),
                                                run.pos_dev[s].data_ptr())

@@ -65,6 +65,45 @@ def _parity_case(name, base, kw):
     _run_lockstep(cfg)
 
 
+APPEND_CASES = {
+    # growing contexts: (base, overrides); R = 0 takes the two-launch path
+    "window_37": (3, dict(B=2, layers=3, L0=6000, C=2500, R=37, k=1000, steps=8)),
+    "window_1": (3, dict(B=3, layers=2, L0=3000, C=900, R=1, k=400, steps=10)),
+    "window_covers_context": (3, dict(B=2, layers=1, L0=40, C=64, R=64, k=32, steps=12)),
+    "no_window": (3, dict(B=2, layers=2, L0=3000, C=900, R=0, k=400, steps=10)),
+    "pages_window": (5, dict(B=2, layers=2, L0=3000, R=3, growth=1, steps=8)),
+}
+
+
+@pytest.mark.parametrize("flags", ["none", "no_io"])
+@pytest.mark.parametrize("mode", ["fused", "split"])
+@pytest.mark.parametrize("name", sorted(APPEND_CASES))
+def test_append_resolve_parity(name, mode, flags, monkeypatch):
+    """hisparse_append_resolve (one launch with a window, two without) equals
+    the oracle's append followed by its step, state and slot bytes."""
+    import torch
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    from tests.gpu_harness import LockstepRun
+    monkeypatch.setenv("HISPARSE_FETCH_MODE", mode)
+    base, kw = APPEND_CASES[name]
+    cfg = WORKLOADS[base].scaled(**kw)
+    fl = hb.HISPARSE_NO_IO if flags == "no_io" else 0
+    print(f"[append_resolve] {name} {mode} {flags}: B={cfg.B} L={cfg.layers} L0={cfg.L0} "
+          f"C={cfg.C} R={cfg.R} k={cfg.k} steps={cfg.steps}", flush=True)
+    run = LockstepRun(cfg, flags=fl)
+    try:
+        for s in range(cfg.steps):
+            if s > 0:
+                run.append_and_step(s)
+            else:
+                run.gpu_step(s)
+            torch.cuda.synchronize()
+            run.compare_step(s, run.oracle_step(s))
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("name", ["mix_window_two_rounds", "pages"])
 def test_parity_reduced_no_io(name):
     base, kw = CASES[name]
