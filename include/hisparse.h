@@ -256,8 +256,11 @@ int hisparse_append(hisparse_t h, hipStream_t stream, int32_t layer, const void*
  * window (R >= 1) the appended position is resident, so the resolution
  * neither looks it up nor fetches it and the row stores run inside the
  * resolve launch; without a window, or when `layer` has a pending prefetch,
- * the two calls are made as separate launches.  Graph-capturable like
- * hisparse_resolve.  Errors: INVALID_ARG, HIP. */
+ * the two calls are made as separate launches.  A pending prefetch has
+ * resolved the layer already: without a window the append must come before
+ * that prefetch (hisparse_append), since the prefetch may fetch the appended
+ * position.  Graph-capturable like hisparse_resolve.  Errors: INVALID_ARG,
+ * HIP. */
 int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, const void* rows,
                             const int32_t* pos, const int32_t* sel, const int32_t* ctx_len,
                             int32_t* out_slot);
