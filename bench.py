@@ -93,6 +93,18 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def host_mem_available_gib():
+    """MemAvailable of /proc/meminfo, GiB (None where unreadable)."""
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return round(int(line.split()[1]) / 2**20, 1)
+    except OSError:
+        pass
+    return None
+
+
 class Setup:
     """Host histories, two library instances (IO and no-IO) and device inputs."""
 
@@ -105,6 +117,9 @@ class Setup:
         t0 = time.time()
         self.trace = make_trace(cfg, queries=queries)                  # [S, L, B, k]
         nbytes = cfg.l_cap * cfg.row_bytes
+        # pinning fails loudly (the binding raises); nothing is shrunk to fit
+        self.host_memory = {"available_before_GiB": host_mem_available_gib(),
+                            "pinned_GiB": round(cfg.streams * nbytes / 2**30, 3)}
         self.hosts = {}
         for l in range(cfg.layers):
             for b in range(cfg.B):
@@ -953,6 +968,7 @@ def main():
                            "hits": tot_hit,
                            "GBps_over_fetch_kernels": round(fetch_gbps, 3),
                            "GBps_over_timed_region": round(miss_bytes / elapsed / 1e9, 3)},
+            "host_memory": setup.host_memory,
             "eager": {"entries_per_s": round(entries / elapsed_eager, 1),
                       "ms_per_step": round(elapsed_eager / K * 1e3, 4),
                       "mode": "eager launches, library HIP-event timing on (the kernel-timing "
