@@ -151,3 +151,10 @@ def test_multi_resolve_rejects_a_null_handle():
     with pytest.raises(hb.HisparseError) as e:
         hb.hisparse_resolve_multi(None, 0, 256, 2, 8, 256, 0, 256)
     assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+
+
+def test_append_resolve_rejects_a_null_handle_and_null_buffers():
+    """Host-side checks of hisparse_append_resolve, before any launch."""
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_append_resolve(None, 0, 0, 256, 256, 256, 256, 256)
+    assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG

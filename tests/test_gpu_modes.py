@@ -379,3 +379,44 @@ def test_timing_counts_every_launch():
         assert t["resolve_ms"] > 0 and t["fetch_ms"] > 0
     finally:
         run.close()
+
+
+def test_append_resolve_argument_checks():
+    """hisparse_append_resolve rejects a bad layer, NULL buffers and
+    misaligned rows before any launch, and leaves the streams untouched."""
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import GpuInstance
+    cfg = WORKLOADS[3].scaled(B=2, layers=2, L0=3000, C=900, R=8, k=400, steps=2)
+    g = GpuInstance(cfg)
+    try:
+        rows = torch.zeros(cfg.B * cfg.row_bytes + 16, dtype=torch.uint8, device="cuda")
+        pos = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device="cuda")
+        sel = torch.full((cfg.B, cfg.k), -1, dtype=torch.int32, device="cuda")
+        ctx = torch.full((cfg.B,), cfg.L0 + 1, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(sel)
+        good = dict(layer=0, rows=rows.data_ptr(), pos=pos.data_ptr(), sel=sel.data_ptr(),
+                    ctx=ctx.data_ptr(), out=out.data_ptr())
+        for bad in (dict(layer=2), dict(layer=-1), dict(rows=0), dict(pos=0), dict(sel=0),
+                    dict(ctx=0), dict(out=0), dict(rows=rows.data_ptr() + 4)):
+            kw = dict(good, **bad)
+            with pytest.raises(hb.HisparseError) as e:
+                hb.hisparse_append_resolve(g.h, g.stream, kw["layer"], kw["rows"], kw["pos"],
+                                           kw["sel"], kw["ctx"], kw["out"])
+            assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG, bad
+        torch.cuda.synchronize()
+        for l in range(cfg.layers):
+            for b in range(cfg.B):
+                assert int(g.hdr(b, l)[hb.HDR_T]) == 0
+        # a well-formed all-padding call: the clock ticks, the row lands
+        rows[:cfg.B * cfg.row_bytes] = 7
+        hb.hisparse_append_resolve(g.h, g.stream, 1, rows.data_ptr(), pos.data_ptr(),
+                                   sel.data_ptr(), ctx.data_ptr(), out.data_ptr())
+        torch.cuda.synchronize()
+        assert (out == -1).all()
+        for b in range(cfg.B):
+            assert int(g.hdr(b, 1)[hb.HDR_T]) == 1
+            assert (g.host(b, 1)[cfg.L0] == 7).all()
+            assert (g.slots(b, 1)[cfg.C + cfg.L0 % cfg.R] == 7).all()
+        assert g.status() == 0
+    finally:
+        g.close()
