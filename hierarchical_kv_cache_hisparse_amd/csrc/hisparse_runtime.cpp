@@ -186,6 +186,23 @@ void release(hisparse* h) {
   delete h;
 }
 
+// true when [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// out_slot is written while sel and ctx_len are still being read
+int check_no_overlap(const hisparse* h, const int32_t* sel, size_t sel_entries,
+                     const int32_t* ctx_len, const int32_t* out) {
+  const size_t B = (size_t)h->cfg.num_requests;
+  const size_t out_bytes = sizeof(int32_t) * sel_entries;
+  if (overlaps(out, out_bytes, sel, sizeof(int32_t) * sel_entries) ||
+      overlaps(out, out_bytes, ctx_len, sizeof(int32_t) * B))
+    return fail(HISPARSE_ERR_INVALID_ARG, "out_slot overlaps sel or ctx_len");
+  return HISPARSE_OK;
+}
+
 int check_device_buffer(const void* p, const char* name) {
   if (!p) return fail(HISPARSE_ERR_INVALID_ARG, "%s is NULL", name);
   if (reinterpret_cast<uintptr_t>(p) % 256 != 0)
@@ -365,6 +382,9 @@ int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel, const
     return fail(HISPARSE_ERR_INVALID_ARG, "sel, ctx_len and out_slot must not be NULL");
   if (layer < 0 || layer >= h->cfg.num_layers)
     return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
+  if (int rc = check_no_overlap(h, sel, (size_t)h->cfg.num_requests * h->cfg.top_k, ctx_len,
+                                out_slot))
+    return rc;
   if (h->pending[layer]) {
     // join the prefetch: wait for it, then hand over its slot map
     HIP_TRY(hipStreamWaitEvent(stream, h->ev_done[layer], 0));
@@ -393,6 +413,8 @@ int hisparse_resolve_multi(hisparse_t h, hipStream_t stream, const int32_t* sel,
     return fail(HISPARSE_ERR_STATE, "layer %d has a pending prefetch: join it with hisparse_resolve",
                 layer);
   const int ke = queries * per_query;
+  if (int rc = check_no_overlap(h, sel, (size_t)h->cfg.num_requests * ke, ctx_len, out_slot))
+    return rc;
   const ResolveShape sh = resolve_shape(h->cfg.top_k, h->cfg.cache_slots,
                                         (h->cfg.flags & HISPARSE_DEBUG_VALIDATE) != 0, ke);
   if (sh.lds_bytes > h->lds_max)
@@ -452,6 +474,9 @@ int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, con
     return fail(HISPARSE_ERR_INVALID_ARG, "layer %d out of range", layer);
   if (reinterpret_cast<uintptr_t>(rows) % 16 != 0)
     return fail(HISPARSE_ERR_INVALID_ARG, "rows must be 16-byte aligned");
+  if (int rc = check_no_overlap(h, sel, (size_t)h->cfg.num_requests * h->cfg.top_k, ctx_len,
+                                out_slot))
+    return rc;
   if (h->cfg.resident_window == 0 || h->pending[layer]) {
     // the appended position may be fetched by this resolve (no window), or the
     // layer was resolved early: the append goes first, in its own launch

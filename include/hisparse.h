@@ -180,7 +180,8 @@ int hisparse_destroy(hisparse_t h);
  *   ctx_len:  device int32 [B]: context length (rows) of each request;
  *   layer:    0 <= layer < num_layers;
  *   out_slot: device int32 [B, k]: slot in [0, C+R) of stream (b, layer)
- *             holding sel[b, i] after the call, -1 for padding.
+ *             holding sel[b, i] after the call, -1 for padding; must not
+ *             overlap sel or ctx_len (INVALID_ARG).
  * One pass per stream does hit detection, LRU victim choice and the
  * metadata update; then (unless HISPARSE_NO_IO) the missing rows are copied
  * from the host history into their slots.  When `layer` was prefetched in
@@ -189,7 +190,7 @@ int hisparse_destroy(hisparse_t h);
  * host-to-device fetches -- inside the decode graph; P2 Timeline: resident,
  * hot and missing rows in a single pass, graph-capturable; P1 Timeline:
  * only the missing top-k rows are copied back.]
- * Errors: INVALID_ARG (NULL pointer, bad layer), HIP. */
+ * Errors: INVALID_ARG (NULL pointer, bad layer, overlapping buffers), HIP. */
 int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel,
                      const int32_t* ctx_len, int32_t layer, int32_t* out_slot);
 
@@ -199,7 +200,8 @@ int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel,
  *             -1 = padding; positions may repeat across and within queries;
  *   queries x per_query <= top_k;
  *   out_slot: device int32 [B, queries, per_query]: the slot holding each
- *             entry's position after the call, -1 for padding.
+ *             entry's position after the call, -1 for padding; must not
+ *             overlap sel or ctx_len.
  * The queries of a step attend through the same cache, so the step resolves
  * the union of their selections once (one clock tick per stream): the union
  * is taken in first-occurrence order over the entries (query-major), every

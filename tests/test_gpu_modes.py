@@ -420,3 +420,31 @@ def test_append_resolve_argument_checks():
         assert g.status() == 0
     finally:
         g.close()
+
+
+def test_overlapping_output_is_rejected():
+    """out_slot sharing bytes with sel or ctx_len is refused on the host (the
+    kernel reads them while it writes out_slot)."""
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import GpuInstance
+    cfg = WORKLOADS[2].scaled(B=2, L0=5000, C=800, R=8, k=256, steps=1)
+    g = GpuInstance(cfg)
+    try:
+        buf = torch.full((3 * cfg.B * cfg.k,), -1, dtype=torch.int32, device="cuda")
+        ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device="cuda")
+        sel = buf[:cfg.B * cfg.k]
+        for out_ptr in (sel.data_ptr(), sel.data_ptr() + 4 * (cfg.B * cfg.k - 1), ctx.data_ptr()):
+            with pytest.raises(hb.HisparseError) as e:
+                hb.hisparse_resolve(g.h, g.stream, sel.data_ptr(), ctx.data_ptr(), 0, out_ptr)
+            assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+            with pytest.raises(hb.HisparseError):
+                hb.hisparse_resolve_multi(g.h, g.stream, sel.data_ptr(), 2, cfg.k // 2,
+                                          ctx.data_ptr(), 0, out_ptr)
+        # adjacent, not overlapping: accepted
+        out = buf[cfg.B * cfg.k: 2 * cfg.B * cfg.k]
+        hb.hisparse_resolve(g.h, g.stream, sel.data_ptr(), ctx.data_ptr(), 0, out.data_ptr())
+        torch.cuda.synchronize()
+        assert (out == -1).all() and int(g.hdr(0, 0)[hb.HDR_T]) == 1
+        assert g.status() == 0
+    finally:
+        g.close()
