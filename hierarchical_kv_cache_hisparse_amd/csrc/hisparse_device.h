@@ -16,6 +16,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// A pointer to device-visible memory (HBM, or pinned host memory mapped into
+// the device address space) in the global address space.  Host-row pointers
+// are read from the handle's pointer table, so the compiler cannot infer
+// their address space and would emit flat instructions; flat loads count in
+// lgkmcnt as well as vmcnt, which makes every later LDS wait also wait for
+// the host round trip.  Accesses through this cast are global_load /
+// global_store, counted in vmcnt only.
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* global_ptr(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts by
 // 1, 2, 4, 8 inside each 16-lane row, then the row totals are carried with
 // the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2

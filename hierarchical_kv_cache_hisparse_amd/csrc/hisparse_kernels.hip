@@ -211,9 +211,10 @@ __global__ void __launch_bounds__(kMaxThreads)
     } else if (pos >= 0) {
       const int cpr = v.row_bytes >> 4;
       const u32x4* src = reinterpret_cast<const u32x4*>(app_rows + (int64_t)b * v.row_bytes);
-      u32x4* hrow = reinterpret_cast<u32x4*>(v.host[layer * v.B + b] + (int64_t)pos * v.row_bytes);
-      u32x4* ring = reinterpret_cast<u32x4*>(
-          v.cache + ((int64_t)(layer * v.B + b) * (C + R) + C + pos % R) * v.row_bytes);
+      auto hrow = global_ptr(
+          reinterpret_cast<u32x4*>(v.host[layer * v.B + b] + (int64_t)pos * v.row_bytes));
+      auto ring = global_ptr(reinterpret_cast<u32x4*>(
+          v.cache + ((int64_t)(layer * v.B + b) * (C + R) + C + pos % R) * v.row_bytes));
       for (int c = tid; c < cpr; c += BD) {
         const u32x4 val = src[c];
         hrow[c] = val;
@@ -239,6 +240,9 @@ __global__ void __launch_bounds__(kMaxThreads)
   }
   const int32_t ctx = ctx_len[b];
   const int32_t t = st.hdr[kHdrT] + 1;  // one clock tick per resolve
+  // the stream's host history (read here, so that the first host reads of the
+  // fused copy do not wait for this pointer)
+  const uint8_t* host = v.host[layer * v.B + b];
   const int64_t tot_miss = *reinterpret_cast<const int64_t*>(st.hdr + kHdrTotalMiss);
   const int64_t tot_evict = *reinterpret_cast<const int64_t*>(st.hdr + kHdrTotalEvict);
   const int64_t tot_hit = *reinterpret_cast<const int64_t*>(st.hdr + kHdrTotalHit);
@@ -394,7 +398,6 @@ __global__ void __launch_bounds__(kMaxThreads)
   const bool fuse = v.fuse_fetch && !(v.flags & HISPARSE_NO_IO);
   const uint32_t cpr = (uint32_t)(v.row_bytes >> 4);
   const uint32_t total = fuse ? (uint32_t)M * cpr : 0u;
-  const uint8_t* host = v.host[layer * v.B + b];
   u32x4 pre_val[kPre > 0 ? kPre : 1];
   uint32_t pre_c[kPre > 0 ? kPre : 1];
   int pre_j[kPre > 0 ? kPre : 1];
@@ -404,8 +407,8 @@ __global__ void __launch_bounds__(kMaxThreads)
     pre_j[u] = -1;
     if (g < total) {
       pre_j[u] = (int)fast_div(g, cpr, v.cpr_magic, &pre_c[u]);
-      pre_val[u] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(host + (int64_t)missp[pre_j[u]] * v.row_bytes) + pre_c[u]);
+      pre_val[u] = __builtin_nontemporal_load(global_ptr(
+          reinterpret_cast<const u32x4*>(host + (int64_t)missp[pre_j[u]] * v.row_bytes) + pre_c[u]));
     }
   }
 
@@ -509,7 +512,7 @@ __global__ void __launch_bounds__(kMaxThreads)
           const uint32_t j = fast_div(g, cpr, v.cpr_magic, &c[u]);
           sl[u] = missi[j];
           val[u] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(host + (int64_t)missp[j] * v.row_bytes) + c[u]);
+              global_ptr(reinterpret_cast<const u32x4*>(host + (int64_t)missp[j] * v.row_bytes) + c[u]));
         }
       }
 #pragma unroll
@@ -572,12 +575,12 @@ __global__ void __launch_bounds__(kFetchThreads) fetch_kernel(StreamView v, int 
         const uint8_t* host = v.host[layer * B + lo];
         dst[u] = v.cache + ((int64_t)(layer * B + lo) * (v.C + v.R) + e.x) * v.row_bytes + 16 * c;
         val[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(host + (int64_t)e.y * v.row_bytes) + c);
+            global_ptr(reinterpret_cast<const u32x4*>(host + (int64_t)e.y * v.row_bytes) + c));
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (dst[u]) *reinterpret_cast<u32x4*>(dst[u]) = val[u];
+      if (dst[u]) *global_ptr(reinterpret_cast<u32x4*>(dst[u])) = val[u];
   }
 }
 
@@ -624,7 +627,7 @@ __global__ void load_window_kernel(StreamView v, int layer0, const int32_t* __re
     const uint32_t r = fast_div(g, cpr, v.cpr_magic, &c);
     const int32_t pos = lo + (int32_t)r;
     const u32x4 val = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(host + (int64_t)pos * v.row_bytes) + c);
+        global_ptr(reinterpret_cast<const u32x4*>(host + (int64_t)pos * v.row_bytes) + c));
     reinterpret_cast<u32x4*>(dst + (int64_t)(v.C + pos % v.R) * v.row_bytes)[c] = val;
   }
 }
@@ -648,7 +651,7 @@ __global__ void append_kernel(StreamView v, int layer, const uint8_t* __restrict
   const u32x4* src = reinterpret_cast<const u32x4*>(rows + (int64_t)b * v.row_bytes);
   for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < cpr; c += gridDim.x * blockDim.x) {
     const u32x4 val = src[c];
-    reinterpret_cast<u32x4*>(host + (int64_t)pos * v.row_bytes)[c] = val;
+    global_ptr(reinterpret_cast<u32x4*>(host + (int64_t)pos * v.row_bytes))[c] = val;
     if (v.R > 0) reinterpret_cast<u32x4*>(dst + (int64_t)(v.C + pos % v.R) * v.row_bytes)[c] = val;
   }
 }
