@@ -80,6 +80,21 @@ __device__ __forceinline__ int64_t row_ctx(const TopkArgs& a, int b) {
 // inside [0, ctx).
 __device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t chunk0,
                                            int64_t ctx, int tid, float (&v)[kTkPerThread]) {
+  if (chunk0 + kTopkChunk <= ctx) {
+    // a whole chunk (every chunk of a row but its last): four 16-byte loads
+    // with no branch between them, so all four are in flight at once (behind
+    // per-lane branches the compiler waits for each before the next)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 x =
+          *reinterpret_cast<const float4*>(row + chunk0 + j * (4 * kTopkThreads) + 4 * tid);
+      v[4 * j + 0] = x.x;
+      v[4 * j + 1] = x.y;
+      v[4 * j + 2] = x.z;
+      v[4 * j + 3] = x.w;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t p0 = chunk0 + j * (4 * kTopkThreads) + 4 * tid;
