@@ -488,18 +488,25 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
 
 def mla_study(setup, K, H):
     """Sparse MLA decode attention over the slot map of layer 0, after each of
-    K resolve steps; timed with torch events on the launching stream.
+    K resolve steps; timed with torch events on the launching stream.  With
+    several query tokens per request (--queries Q) every token attends to its
+    own entries of the multi-query slot map.
 
-    Algorithmic bytes per call: the attended rows (B * k * T * 1152), the
-    queries, outputs and lse; FLOPs: 2 * B * H * k * T * (576 + 512)."""
+    Algorithmic bytes per call: the attended rows (B * Q * k_q * T * 1152),
+    the queries, outputs and lse; FLOPs: 2 * B * Q * H * k_q * T * (576 + 512)."""
     torch, hb, cfg = setup.torch, setup.hb, setup.cfg
     from workload.rows import make_queries
     io = setup.io
     T = cfg.row_bytes // 1152
-    ws = torch.empty(hb.hisparse_mla_workspace_bytes(io.h, H), dtype=torch.uint8, device="cuda:0")
-    q = torch.from_numpy(make_queries(cfg.B, H, 3000 + cfg.data_seed, 0)).to("cuda:0")
-    out = torch.empty((cfg.B, H, 512), dtype=torch.float32, device="cuda:0")
-    lse = torch.empty((cfg.B, H), dtype=torch.float32, device="cuda:0")
+    Q = setup.queries               # query tokens per request (rows of attention)
+    per = cfg.k // Q
+    rows = cfg.B * Q
+    ws = torch.empty(hb.hisparse_mla_workspace_bytes_multi(io.h, Q, per, H), dtype=torch.uint8,
+                     device="cuda:0")
+    q_np = make_queries(rows, H, 3000 + cfg.data_seed, 0)
+    q = torch.from_numpy(q_np).to("cuda:0")
+    out = torch.empty((rows, H, 512), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((rows, H), dtype=torch.float32, device="cuda:0")
     scale = 1.0 / np.sqrt(576.0)
     stream = torch.cuda.current_stream().cuda_stream
     setup.reset(io)
@@ -508,8 +515,13 @@ def mla_study(setup, K, H):
         setup.step(io, s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        hb.hisparse_sparse_mla_decode(io.h, stream, 0, q.data_ptr(), setup.out[0].data_ptr(), H,
-                                      scale, ws.data_ptr(), out.data_ptr(), lse.data_ptr())
+        if Q == 1:
+            hb.hisparse_sparse_mla_decode(io.h, stream, 0, q.data_ptr(), setup.out[0].data_ptr(),
+                                          H, scale, ws.data_ptr(), out.data_ptr(), lse.data_ptr())
+        else:
+            hb.hisparse_sparse_mla_decode_multi(io.h, stream, 0, Q, per, q.data_ptr(),
+                                                setup.out[0].data_ptr(), H, scale, ws.data_ptr(),
+                                                out.data_ptr(), lse.data_ptr())
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) * 1e3)
@@ -517,38 +529,40 @@ def mla_study(setup, K, H):
     # the float64 oracle attention on the host, over the host rows at the last
     # step's selections, for as many requests as fit ~10 s (at least one)
     from oracle.attention import bf16_to_f64, mla_decode_attention_lse
-    q_np = make_queries(cfg.B, H, 3000 + cfg.data_seed, 0)
     t_cpu, n_cpu = 0.0, 0
-    for b in range(cfg.B):
-        sel = setup.trace[K - 1, 0, b]
+    for r in range(rows):
+        b, j = divmod(r, Q)
+        sel = setup.trace[K - 1, 0, b].reshape(Q, per)[j]
         host = setup.hosts[(b, 0)][1]
-        rows = host[sel[sel >= 0]].reshape(-1, 1152)
+        tok = host[sel[sel >= 0]].reshape(-1, 1152)
         t0 = time.perf_counter()
-        mla_decode_attention_lse(bf16_to_f64(q_np[b]), bf16_to_f64(rows), scale)
+        mla_decode_attention_lse(bf16_to_f64(q_np[r]), bf16_to_f64(tok), scale)
         t_cpu += time.perf_counter() - t0
         n_cpu += 1
         if t_cpu > 10.0:
             break
-    cpu_us_per_call = t_cpu / n_cpu * cfg.B * 1e6
-    n_tok = cfg.k * T
-    byts = cfg.B * n_tok * 1152 + cfg.B * H * (1152 + 512 * 4 + 4)
-    flops = 2.0 * cfg.B * H * n_tok * (576 + 512)
+    cpu_us_per_call = t_cpu / n_cpu * rows * 1e6
+    n_tok = per * T
+    byts = rows * n_tok * 1152 + rows * H * (1152 + 512 * 4 + 4)
+    flops = 2.0 * rows * H * n_tok * (576 + 512)
     return {"metric": "sparse MLA decode attention over the slot map", "value": round(us, 3),
             "unit": "us per layer call", "higher_is_better": False, "workload": cfg.name,
-            "requests": cfg.B, "heads": H, "attended_rows_per_request": n_tok,
+            "requests": cfg.B, "query_tokens_per_request": Q, "heads": H,
+            "attended_rows_per_query_token": n_tok,
             "roofline": {"bound": "hbm", "kernel": "mla_decode_kernel + mla_combine_kernel",
                          "achieved": round(byts / us / 1e3, 1), "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": round(byts / us / 1e3 / HBM_PEAK_GBPS, 4),
                          "per_launch_bytes": byts,
                          **traffic_fields(committed_traffic(
-                             ("mla_decode_kernel", "mla_combine_kernel"), f"{cfg.label}_h{H}", "mla"))},
+                             ("mla_decode_kernel", "mla_combine_kernel"),
+                             f"{cfg.label}_h{H}" + (f"_q{Q}" if Q > 1 else ""), "mla"))},
             "mfma": {"achieved_TFLOPs": round(flops / us / 1e6, 2), "peak_TFLOPs": 2500.0,
                      "frac": round(flops / us / 1e6 / 2500.0, 5)},
             "timing": "torch events around each launch, median of steps 1..",
             "cpu_baseline": {"value": round(cpu_us_per_call, 1), "unit": "us per layer call",
                              "cores": 1, "kind": "oracle",
-                             "sample": f"float64 numpy oracle on {n_cpu} of {cfg.B} requests of the "
-                                       f"last step, scaled to all requests"}}
+                             "sample": f"float64 numpy oracle on {n_cpu} of {rows} attention rows "
+                                       f"of the last step, scaled to all rows"}}
 
 
 def topk_study(cfg, K, W):

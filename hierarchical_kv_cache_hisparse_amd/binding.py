@@ -113,6 +113,9 @@ def library():
             "hisparse_probe_host_read": [P, P, P, SZ, I32],
             "hisparse_mla_workspace_bytes": [P, I32, P],
             "hisparse_sparse_mla_decode": [P, P, I32, P, P, I32, ctypes.c_float, P, P, P],
+            "hisparse_mla_workspace_bytes_multi": [P, I32, I32, I32, P],
+            "hisparse_sparse_mla_decode_multi": [P, P, I32, I32, I32, P, P, I32, ctypes.c_float, P,
+                                                 P, P],
             "hisparse_topk_workspace_bytes": [I32, ctypes.c_int64, P],
             "hisparse_topk": [P, P, ctypes.c_int64, I32, ctypes.c_int64, P, I32, P, P],
         }
@@ -258,6 +261,23 @@ def hisparse_sparse_mla_decode(h, stream: int, layer: int, q: int, out_slot: int
     _check(library().hisparse_sparse_mla_decode(h, stream, layer, q, out_slot, num_heads,
                                                 scale, workspace, out, lse),
            "hisparse_sparse_mla_decode")
+
+
+def hisparse_mla_workspace_bytes_multi(h, queries: int, per_query: int, num_heads: int) -> int:
+    n = ctypes.c_size_t()
+    _check(library().hisparse_mla_workspace_bytes_multi(h, queries, per_query, num_heads,
+                                                        ctypes.byref(n)),
+           "hisparse_mla_workspace_bytes_multi")
+    return n.value
+
+
+def hisparse_sparse_mla_decode_multi(h, stream: int, layer: int, queries: int, per_query: int,
+                                     q: int, out_slot: int, num_heads: int, scale: float,
+                                     workspace: int, out: int, lse: int) -> None:
+    _check(library().hisparse_sparse_mla_decode_multi(h, stream, layer, queries, per_query, q,
+                                                      out_slot, num_heads, scale, workspace, out,
+                                                      lse),
+           "hisparse_sparse_mla_decode_multi")
 
 
 def hisparse_topk_workspace_bytes(num_rows: int, max_len: int) -> int:

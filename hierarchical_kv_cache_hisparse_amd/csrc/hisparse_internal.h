@@ -151,12 +151,13 @@ struct MlaArgs {
   int64_t row_bytes;          // bytes per slot
   int32_t slots_total;        // C + R
   int32_t T;                  // token rows per slot
-  int32_t k;                  // slot-map entries per request
-  int32_t B;                  // requests
+  int32_t k;                  // slot-map entries per attention row
+  int32_t B;                  // attention rows (requests x query tokens)
+  int32_t Qn;                 // attention rows per request: row r reads stream r / Qn
   int32_t H, HBn, S;          // heads, head blocks, splits of the token rows
   int32_t rows_per_split;     // multiple of 64
   float scale;
-  const __bf16* q;            // [B, H, 576]
+  const __bf16* q;            // [B, H, 576] (B attention rows)
   const int32_t* slots;       // [B, k]
   float* part;                // [B * HBn * S][16][512] partial outputs
   float* part_ml;             // [B * HBn * S][16][2] partial (max, sum)

@@ -8,6 +8,11 @@
 // Abstract: outputs unchanged; "Hybrid HiSparse", Timeline: the method sits
 // under sparse MLA decoding).
 //
+// Several query tokens per request (multi-token prediction): attention row
+// r = b * Qn + q is query token q of request b; it has its own queries and
+// slot-map entries (row r of the multi-query slot map) and reads request b's
+// slot rows.
+//
 // Row format: a token row is 576 bf16, 512 compressed-latent values (shared
 // by keys and values) followed by 64 rope values (key only).  A slot holds
 // T = row_bytes / 1152 token rows (T = 16 for Quest-style pages); every token
@@ -121,7 +126,7 @@ mla_decode_kernel(MlaArgs a) {
   const int r_begin = split * a.rows_per_split;
   const int r_end = min(n_tok, r_begin + a.rows_per_split);
   const int32_t* slots = a.slots + (int64_t)b * a.k;
-  const uint8_t* cbase = a.cache + (int64_t)b * a.stream_bytes;
+  const uint8_t* cbase = a.cache + (int64_t)(b / a.Qn) * a.stream_bytes;  // the row's request
   const bf16x8 zero8 = {};
 
   // The wave's 16 rows of a tile are read with whole 128-byte lines per

@@ -573,21 +573,36 @@ int check_mla(const hisparse* h, int32_t num_heads) {
 }
 }  // namespace
 
-int hisparse_mla_workspace_bytes(hisparse_t h, int32_t num_heads, size_t* bytes) {
+namespace {
+// queries x per_query attention rows' entries must fit a slot-map row
+int check_mla_rows(const hisparse* h, int32_t queries, int32_t per_query) {
+  if (queries < 1 || per_query < 1 || (int64_t)queries * per_query > h->cfg.top_k)
+    return fail(HISPARSE_ERR_INVALID_ARG,
+                "queries (%d) x per_query (%d) must be in [1, top_k = %d]", queries, per_query,
+                h->cfg.top_k);
+  if ((int64_t)h->cfg.num_requests * queries > 65535)
+    return fail(HISPARSE_ERR_UNSUPPORTED, "more than 65535 attention rows");
+  return HISPARSE_OK;
+}
+
+int mla_bytes(hisparse_t h, int32_t queries, int32_t per_query, int32_t num_heads,
+              size_t* bytes) {
   int rc = check_mla(h, num_heads);
   if (rc) return rc;
+  if ((rc = check_mla_rows(h, queries, per_query))) return rc;
   if (!bytes) return fail(HISPARSE_ERR_INVALID_ARG, "bytes is NULL");
-  const MlaShape sh = mla_shape(h->cfg.num_requests, num_heads, h->cfg.top_k,
+  const MlaShape sh = mla_shape(h->cfg.num_requests * queries, num_heads, per_query,
                                 h->cfg.row_bytes / (2 * kMlaDqk));
   *bytes = mla_workspace(sh).total;
   return HISPARSE_OK;
 }
 
-int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, const void* q,
-                               const int32_t* out_slot, int32_t num_heads, float scale,
-                               void* workspace, float* out, float* lse) {
+int mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, int32_t queries,
+               int32_t per_query, const void* q, const int32_t* out_slot, int32_t num_heads,
+               float scale, void* workspace, float* out, float* lse) {
   int rc = check_mla(h, num_heads);
   if (rc) return rc;
+  if ((rc = check_mla_rows(h, queries, per_query))) return rc;
   if (layer < 0 || layer >= h->cfg.num_layers)
     return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
   if (!q || !out_slot || !workspace || !out || !lse)
@@ -595,8 +610,9 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
   if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(HISPARSE_ERR_INVALID_ARG, "q must be 16-byte and workspace 256-byte aligned");
   const int B = h->cfg.num_requests;
+  const int rows = B * queries;
   const int T = h->cfg.row_bytes / (2 * kMlaDqk);
-  const MlaShape sh = mla_shape(B, num_heads, h->cfg.top_k, T);
+  const MlaShape sh = mla_shape(rows, num_heads, per_query, T);
   const MlaWorkspace ws = mla_workspace(sh);
   uint8_t* w = static_cast<uint8_t*>(workspace);
   MlaArgs a{};
@@ -607,8 +623,9 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
   a.row_bytes = h->cfg.row_bytes;
   a.slots_total = h->cfg.cache_slots + h->cfg.resident_window;
   a.T = T;
-  a.k = h->cfg.top_k;
-  a.B = B;
+  a.k = per_query;
+  a.B = rows;
+  a.Qn = queries;
   a.H = num_heads;
   a.HBn = sh.HBn;
   a.S = sh.S;
@@ -622,6 +639,35 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
   a.lse = lse;
   HIP_TRY(launch_mla(a, stream, sh.lds_bytes));
   return HISPARSE_OK;
+}
+}  // namespace
+
+int hisparse_mla_workspace_bytes(hisparse_t h, int32_t num_heads, size_t* bytes) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  return mla_bytes(h, 1, h->cfg.top_k, num_heads, bytes);
+}
+
+int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, const void* q,
+                               const int32_t* out_slot, int32_t num_heads, float scale,
+                               void* workspace, float* out, float* lse) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  return mla_decode(h, stream, layer, 1, h->cfg.top_k, q, out_slot, num_heads, scale, workspace,
+                    out, lse);
+}
+
+int hisparse_mla_workspace_bytes_multi(hisparse_t h, int32_t queries, int32_t per_query,
+                                       int32_t num_heads, size_t* bytes) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  return mla_bytes(h, queries, per_query, num_heads, bytes);
+}
+
+int hisparse_sparse_mla_decode_multi(hisparse_t h, hipStream_t stream, int32_t layer,
+                                     int32_t queries, int32_t per_query, const void* q,
+                                     const int32_t* out_slot, int32_t num_heads, float scale,
+                                     void* workspace, float* out, float* lse) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  return mla_decode(h, stream, layer, queries, per_query, q, out_slot, num_heads, scale,
+                    workspace, out, lse);
 }
 
 namespace {

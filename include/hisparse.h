@@ -323,6 +323,28 @@ int hisparse_sparse_mla_decode(hisparse_t h, hipStream_t stream, int32_t layer, 
                                const int32_t* out_slot, int32_t num_heads, float scale,
                                void* workspace, float* out, float* lse);
 
+/* The same attention for several query tokens per request (multi-token
+ * prediction), over the slot map hisparse_resolve_multi wrote: query token
+ * j of request b attends to the slots of its own entries, row (b, j) of the
+ * [B, queries, per_query] map, read from request b's cache rows.
+ *   q:        device bf16 [B, queries, num_heads, 576];
+ *   out_slot: device int32 [B, queries, per_query];
+ *   out:      device fp32 [B, queries, num_heads, 512];
+ *   lse:      device fp32 [B, queries, num_heads].
+ * queries x per_query <= top_k and B x queries <= 65535; the workspace size
+ * comes from hisparse_mla_workspace_bytes_multi with the same queries,
+ * per_query and num_heads.  With queries = 1 and per_query = top_k these are
+ * hisparse_mla_workspace_bytes and hisparse_sparse_mla_decode.
+ * [P2 Timeline: multi-token prediction among the features the method works
+ * with.]  Errors: as hisparse_sparse_mla_decode, and INVALID_ARG for
+ * queries or per_query out of range. */
+int hisparse_mla_workspace_bytes_multi(hisparse_t h, int32_t queries, int32_t per_query,
+                                       int32_t num_heads, size_t* bytes);
+int hisparse_sparse_mla_decode_multi(hisparse_t h, hipStream_t stream, int32_t layer,
+                                     int32_t queries, int32_t per_query, const void* q,
+                                     const int32_t* out_slot, int32_t num_heads, float scale,
+                                     void* workspace, float* out, float* lse);
+
 /* ---- top-k selection over indexer scores ----------------------------------
  * The step before resolution: from one score per position (a token for
  * DSA-style per-layer selection, a 16-token page for Quest-style selection),

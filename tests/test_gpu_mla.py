@@ -164,3 +164,88 @@ def test_attention_graph_replays_are_bit_reproducible():
         attn.check(0, 0)
     finally:
         run.close()
+
+
+MULTI_CASES = {
+    # name: (base workload, query tokens, overrides); k = tokens x per-token count
+    "tokens_two": (2, 2, dict(B=3, L0=8192, C=1500, k=1200, steps=3)),
+    "tokens_three_shared_layers": (4, 3, dict(B=2, layers=2, L0=20000, k=1536, steps=2)),
+    "pages_four": (5, 4, dict(B=2, layers=1, L0=3000, C=300, k=160, steps=3)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_CASES))
+def test_attention_multi_query(name):
+    """Several query tokens per request over the multi-query slot map: token
+    j of request b attends to the slots of its own selections, and equals the
+    float64 oracle over the host rows at those positions."""
+    import torch
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    from tests.gpu_harness import LockstepRun
+    from workload.rows import make_queries
+    base, Q, kw = MULTI_CASES[name]
+    cfg = WORKLOADS[base].scaled(**kw)
+    H, per = 16, cfg.k // Q
+    print(f"[mla multi] {name}: B={cfg.B} Q={Q} per_query={per} H={H}", flush=True)
+    run = LockstepRun(cfg, oracle_streams=[], queries=Q)
+    try:
+        ws = torch.empty(hb.hisparse_mla_workspace_bytes_multi(run.gpu.h, Q, per, H),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((cfg.B * Q, H, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((cfg.B * Q, H), dtype=torch.float32, device="cuda")
+        scale = 1.0 / np.sqrt(576.0)
+        for s in range(cfg.steps):
+            run.gpu_step(s)
+            for l in range(cfg.layers):
+                q_bytes = make_queries(cfg.B * Q, H, 3100 + cfg.data_seed, l)
+                q = torch.from_numpy(q_bytes).to("cuda")
+                hb.hisparse_sparse_mla_decode_multi(
+                    run.gpu.h, torch.cuda.current_stream().cuda_stream, l, Q, per, q.data_ptr(),
+                    run.out_dev[l].data_ptr(), H, scale, ws.data_ptr(), out.data_ptr(),
+                    lse.data_ptr())
+                torch.cuda.synchronize()
+                o, g = out.cpu().numpy(), lse.cpu().numpy()
+                for b in range(cfg.B):
+                    sel_q = run.trace[s, l, b].reshape(Q, per)
+                    for j in range(Q):
+                        r = b * Q + j
+                        ref, ref_lse = _reference(cfg, run.gpu.host(b, l), sel_q[j], q_bytes[r],
+                                                  scale)
+                        err = np.abs(o[r] - ref).max()
+                        assert err <= OUT_ATOL, f"step {s} layer {l} request {b} token {j}: {err}"
+                        np.testing.assert_allclose(g[r], ref_lse, atol=LSE_ATOL, rtol=0)
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+
+
+def test_attention_multi_with_one_token_is_the_single_call():
+    """queries = 1, per_query = top_k: the multi entry is the single-token
+    attention, bit for bit."""
+    import torch
+    from hierarchical_kv_cache_hisparse_amd import binding as hb
+    from tests.gpu_harness import LockstepRun
+    cfg = WORKLOADS[2].scaled(B=3, L0=6000, C=1024, k=512, steps=1)
+    run = LockstepRun(cfg, oracle_streams=[])
+    attn = Attn(run, 32)
+    try:
+        run.gpu_step(0)
+        torch.cuda.synchronize()
+        attn.launch(0, run.out_dev[0])
+        torch.cuda.synchronize()
+        want, want_lse = attn.out.clone(), attn.lse.clone()
+        assert hb.hisparse_mla_workspace_bytes_multi(run.gpu.h, 1, cfg.k, 32) == \
+            hb.hisparse_mla_workspace_bytes(run.gpu.h, 32)
+        attn.out.zero_()
+        hb.hisparse_sparse_mla_decode_multi(
+            run.gpu.h, torch.cuda.current_stream().cuda_stream, 0, 1, cfg.k, attn.q[0].data_ptr(),
+            run.out_dev[0].data_ptr(), 32, attn.scale, attn.ws.data_ptr(), attn.out.data_ptr(),
+            attn.lse.data_ptr())
+        torch.cuda.synchronize()
+        assert torch.equal(attn.out, want) and torch.equal(attn.lse, want_lse)
+        for bad in ((0, 16), (2, 0), (3, cfg.k)):
+            with pytest.raises(hb.HisparseError) as e:
+                hb.hisparse_mla_workspace_bytes_multi(run.gpu.h, bad[0], bad[1], 32)
+            assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+    finally:
+        run.close()
