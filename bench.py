@@ -239,9 +239,11 @@ CSRC = os.path.join(ROOT, "hierarchical_kv_cache_hisparse_amd", "csrc")
 # the sources each kernel family is built from; a counter summary is used only
 # while the hash of its family's sources matches the one it recorded
 SOURCE_FAMILIES = {
-    "resolve": ("hisparse_kernels.hip", "hisparse_device.h", "hisparse_internal.h"),
-    "mla": ("hisparse_mla.hip", "hisparse_device.h", "hisparse_internal.h"),
-    "topk": ("hisparse_topk.hip", "hisparse_device.h", "hisparse_internal.h"),
+    "resolve": ("hisparse_kernels.hip", "hisparse_device.h", "hisparse_internal.h",
+                "hisparse_align.h"),
+    "mla": ("hisparse_mla.hip", "hisparse_device.h", "hisparse_mla_internal.h"),
+    "topk": ("hisparse_topk.hip", "hisparse_device.h", "hisparse_topk_internal.h",
+             "hisparse_align.h"),
 }
 SHA_LINE = {"resolve": "Kernel source sha256[:16]", "mla": "MLA kernel source sha256[:16]",
             "topk": "Top-k kernel source sha256[:16]"}
@@ -289,6 +291,10 @@ def calibration_copy():
     del src, dst
 
 
+KERNEL_NAMES = ("mla_decode_kernel", "mla_combine_kernel", "topk_hist_kernel", "topk_filter_kernel",
+                "topk_finish_kernel", "resolve_kernel", "fetch_kernel")
+
+
 def short_kernel_name(name):
     for key in ("mla_decode_kernel", "mla_combine_kernel", "topk_hist_kernel", "topk_filter_kernel",
                 "topk_finish_kernel", "resolve_kernel", "fetch_kernel",
@@ -305,7 +311,7 @@ def summarize_rocprof(directory, label, command):
     import csv
     import glob
     lines = [f"# {label}", "", f"Command: `{command}`", ""]
-    lines += [f"{SHA_LINE[fam]}: {kernel_source_sha(fam)}" for fam in SOURCE_FAMILIES] + [""]
+    sha_at = len(lines)  # the hashes of the kernel families measured here go here
     stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
     trace = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
     pmc = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
@@ -348,6 +354,10 @@ def summarize_rocprof(directory, label, command):
         for (k, c), v in sorted(agg.items()):
             lines.append(f"pmc: kernel={k} counter={c} mean={sum(v) / len(v):.3f} "
                          f"dispatches={len(v)}")
+    measured = {kernel_family(k) for k in KERNEL_NAMES
+                if any(f"| {k} |" in line or f"kernel={k} " in line for line in lines)}
+    lines[sha_at:sha_at] = [f"{SHA_LINE[fam]}: {kernel_source_sha(fam)}"
+                            for fam in SOURCE_FAMILIES if fam in measured] + [""]
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, label + ".md")
     with open(out, "w") as f:

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "hisparse.h"
+#include "hisparse_align.h"
 
 namespace hsp {
 
@@ -34,7 +35,6 @@ constexpr int kMaxRequests = 32768;   // the fetch kernel keeps B+1 prefixes in 
 constexpr size_t kMaxLdsBytes = 163840;   // gfx950: 160 KiB of LDS per workgroup
 constexpr int kFetchThreads = 256;
 
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte layout of the metadata buffer (mirrors hisparse_meta_layout).
 inline hisparse_meta_layout meta_layout(const hisparse_config& c) {
@@ -104,73 +104,5 @@ hipError_t launch_append(const StreamView& v, hipStream_t s, int layer, const ui
                          const int32_t* pos);
 hipError_t launch_probe_host_read(hipStream_t s, const void* host, void* dev, size_t bytes,
                                   int workgroups);
-
-// ---- top-k selection over indexer scores ---------------------------------------
-constexpr int kTopkChunk = 4096;          // positions per workgroup of the scan kernels
-constexpr int kTopkThreads = 256;         // threads of the scan kernels
-constexpr int kTopkBins = 4096;           // level-1 histogram: top 12 key bits
-constexpr int kTopkCntStride = 64;        // candidate counter words per row
-constexpr int kTopkMaxRows = 65535;       // grid.y of the scan kernels
-constexpr int64_t kTopkMaxLen = (int64_t(1) << 31) - kTopkChunk;
-
-struct TopkArgs {
-  const float* scores;    // [rows][row_stride]
-  int64_t row_stride;     // floats between rows (multiple of 4)
-  int64_t max_len;        // positions per row the workspace is sized for
-  const int32_t* ctx_len; // [rows]: eligible positions [0, ctx), clamped
-  int32_t k;
-  int32_t rows;
-  uint32_t* hist;         // [rows][4096] top-12-bit counts, zero between calls
-  uint32_t* hist2;        // [rows][4096] next-12-bit counts of the candidates, zero between calls
-  uint32_t* cnt;          // [rows][64] counters and the threshold, zero between calls
-  uint32_t* bitmap;       // [rows][bm_words]
-  int64_t bm_words;
-  uint32_t* cand;         // [rows][max_len][2]: (key, position)
-  int32_t* out;           // [rows][k]
-};
-
-struct TopkLayout {
-  size_t hist, hist2, cnt, bitmap, cand, total;  // byte offsets in the workspace
-  int64_t bm_words;
-};
-
-TopkLayout topk_layout(int rows, int64_t max_len);
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
-
-// ---- sparse MLA decode attention over the slot map ----------------------------
-constexpr int kMlaDqk = 576;        // latent 512 + rope 64 (bf16)
-constexpr int kMlaDv = 512;         // value = the latent part
-constexpr int kMlaHB = 16;          // heads per workgroup
-constexpr int kMlaWaves = 4;
-constexpr int kMlaThreads = 64 * kMlaWaves;
-constexpr int kMlaMaxSplits = 256;
-
-struct MlaArgs {
-  const uint8_t* cache;       // slot rows of (request 0, layer)
-  int64_t stream_bytes;       // bytes between consecutive requests' slot rows
-  int64_t row_bytes;          // bytes per slot
-  int32_t slots_total;        // C + R
-  int32_t T;                  // token rows per slot
-  int32_t k;                  // slot-map entries per attention row
-  int32_t B;                  // attention rows (requests x query tokens)
-  int32_t Qn;                 // attention rows per request: row r reads stream r / Qn
-  int32_t H, HBn, S;          // heads, head blocks, splits of the token rows
-  int32_t rows_per_split;     // multiple of 64
-  float scale;
-  const __bf16* q;            // [B, H, 576] (B attention rows)
-  const int32_t* slots;       // [B, k]
-  float* part;                // [B * HBn * S][16][512] partial outputs
-  float* part_ml;             // [B * HBn * S][16][2] partial (max, sum)
-  float* out;                 // [B, H, 512]
-  float* lse;                 // [B, H]
-};
-
-struct MlaShape {
-  int HBn, S, rows_per_split;
-  size_t lds_bytes, part_floats, ml_floats, counters;
-};
-
-MlaShape mla_shape(int B, int H, int k, int T);
-hipError_t launch_mla(const MlaArgs& a, hipStream_t s, size_t lds_bytes);
 
 }  // namespace hsp

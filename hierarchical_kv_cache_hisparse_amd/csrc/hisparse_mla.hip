@@ -57,7 +57,7 @@
 #include <math.h>
 
 #include "hisparse_device.h"
-#include "hisparse_internal.h"
+#include "hisparse_mla_internal.h"
 
 namespace hsp {
 namespace {

@@ -19,6 +19,8 @@
 
 #include "hisparse.h"
 #include "hisparse_internal.h"
+#include "hisparse_mla_internal.h"
+#include "hisparse_topk_internal.h"
 
 using namespace hsp;
 

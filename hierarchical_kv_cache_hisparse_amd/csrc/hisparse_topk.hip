@@ -35,7 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include "hisparse_device.h"
-#include "hisparse_internal.h"
+#include "hisparse_topk_internal.h"
 
 namespace hsp {
 namespace {
