@@ -159,14 +159,18 @@ class Setup:
         hb, cfg = self.hb, self.cfg
         st = self.torch.cuda.current_stream().cuda_stream if stream is None else stream
         for l in range(cfg.layers):
-            if cfg.growth and s > 0 and self.queries == 1:
-                # the decode step of a growing context: append + resolve, one call
-                hb.hisparse_append_resolve(inst.h, st, l, self.rows[s, l].data_ptr(),
-                                           self.pos[s].data_ptr(), self.sel[s, l].data_ptr(),
-                                           self.ctx[s].data_ptr(), self.out[l].data_ptr())
-                continue
             if cfg.growth and s > 0:
-                hb.hisparse_append(inst.h, st, l, self.rows[s, l].data_ptr(), self.pos[s].data_ptr())
+                # the decode step of a growing context: append + resolve, one call
+                if self.queries > 1:
+                    hb.hisparse_append_resolve_multi(
+                        inst.h, st, l, self.rows[s, l].data_ptr(), self.pos[s].data_ptr(),
+                        self.sel[s, l].data_ptr(), self.queries, cfg.k // self.queries,
+                        self.ctx[s].data_ptr(), self.out[l].data_ptr())
+                else:
+                    hb.hisparse_append_resolve(inst.h, st, l, self.rows[s, l].data_ptr(),
+                                               self.pos[s].data_ptr(), self.sel[s, l].data_ptr(),
+                                               self.ctx[s].data_ptr(), self.out[l].data_ptr())
+                continue
             if self.queries > 1:
                 hb.hisparse_resolve_multi(inst.h, st, self.sel[s, l].data_ptr(), self.queries,
                                           cfg.k // self.queries, self.ctx[s].data_ptr(), l,
@@ -1056,9 +1060,8 @@ def main():
             result["no_io"] = {"us_per_layer_call": round(per_call_us, 3),
                                "resolve_kernel_us": round(noio_kernel_us, 3),
                                "includes_append": bool(cfg.growth),
-                               "append": ("fused into the resolve launch (hisparse_append_resolve)"
-                                          if cfg.growth and Q == 1 and cfg.R > 0 else
-                                          "separate launch" if cfg.growth else None),
+                               "append": ("fused into the resolve launch" if cfg.growth and cfg.R > 0
+                                          else "separate launch" if cfg.growth else None),
                                "target_us": budget_us,
                                "frac_of_decode_step_budget": round(
                                    per_call_us / (DECODE_STEP_BUDGET_US / BUDGET_LAYERS), 5),

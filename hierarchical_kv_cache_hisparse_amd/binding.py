@@ -106,6 +106,7 @@ def library():
             "hisparse_load_window": [P, P, I32, P],
             "hisparse_append": [P, P, I32, P, P],
             "hisparse_append_resolve": [P, P, I32, P, P, P, P, P],
+            "hisparse_append_resolve_multi": [P, P, I32, P, P, P, I32, I32, P, P],
             "hisparse_reset": [P, P, I32, I32],
             "hisparse_get_status": [P, P, ctypes.c_int],
             "hisparse_set_timing": [P, ctypes.c_int],
@@ -210,6 +211,14 @@ def hisparse_append_resolve(h, stream: int, layer: int, rows: int, pos: int, sel
                             ctx_len: int, out_slot: int) -> None:
     _check(library().hisparse_append_resolve(h, stream, layer, rows, pos, sel, ctx_len, out_slot),
            "hisparse_append_resolve")
+
+
+def hisparse_append_resolve_multi(h, stream: int, layer: int, rows: int, pos: int, sel: int,
+                                  queries: int, per_query: int, ctx_len: int,
+                                  out_slot: int) -> None:
+    _check(library().hisparse_append_resolve_multi(h, stream, layer, rows, pos, sel, queries,
+                                                   per_query, ctx_len, out_slot),
+           "hisparse_append_resolve_multi")
 
 
 def hisparse_reset(h, stream: int, layer: int = -1, request: int = -1) -> None:

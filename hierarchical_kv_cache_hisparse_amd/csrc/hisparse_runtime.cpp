@@ -205,6 +205,33 @@ int check_no_overlap(const hisparse* h, const int32_t* sel, size_t sel_entries,
   return HISPARSE_OK;
 }
 
+// the host-side checks of a multi-query resolve
+int check_multi(const hisparse* h, const int32_t* sel, int32_t queries, int32_t per_query,
+                const int32_t* ctx_len, int32_t layer, const int32_t* out_slot) {
+  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
+  if (!sel || !ctx_len || !out_slot)
+    return fail(HISPARSE_ERR_INVALID_ARG, "sel, ctx_len and out_slot must not be NULL");
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
+  if (queries < 1 || per_query < 1 || (int64_t)queries * per_query > h->cfg.top_k)
+    return fail(HISPARSE_ERR_INVALID_ARG,
+                "queries (%d) x per_query (%d) must be in [1, top_k = %d]", queries, per_query,
+                h->cfg.top_k);
+  if (h->pending[layer])
+    return fail(HISPARSE_ERR_STATE, "layer %d has a pending prefetch: join it with hisparse_resolve",
+                layer);
+  const int ke = queries * per_query;
+  if (int rc = check_no_overlap(h, sel, (size_t)h->cfg.num_requests * ke, ctx_len, out_slot))
+    return rc;
+  const ResolveShape sh = resolve_shape(h->cfg.top_k, h->cfg.cache_slots,
+                                        (h->cfg.flags & HISPARSE_DEBUG_VALIDATE) != 0, ke);
+  if (sh.lds_bytes > h->lds_max)
+    return fail(HISPARSE_ERR_UNSUPPORTED,
+                "C=%d with %d entries per request needs %zu bytes of LDS; the device has %zu",
+                h->cfg.cache_slots, ke, sh.lds_bytes, h->lds_max);
+  return HISPARSE_OK;
+}
+
 int check_device_buffer(const void* p, const char* name) {
   if (!p) return fail(HISPARSE_ERR_INVALID_ARG, "%s is NULL", name);
   if (reinterpret_cast<uintptr_t>(p) % 256 != 0)
@@ -402,28 +429,9 @@ int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel, const
 int hisparse_resolve_multi(hisparse_t h, hipStream_t stream, const int32_t* sel,
                            int32_t queries, int32_t per_query, const int32_t* ctx_len,
                            int32_t layer, int32_t* out_slot) {
-  if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
-  if (!sel || !ctx_len || !out_slot)
-    return fail(HISPARSE_ERR_INVALID_ARG, "sel, ctx_len and out_slot must not be NULL");
-  if (layer < 0 || layer >= h->cfg.num_layers)
-    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
-  if (queries < 1 || per_query < 1 || (int64_t)queries * per_query > h->cfg.top_k)
-    return fail(HISPARSE_ERR_INVALID_ARG,
-                "queries (%d) x per_query (%d) must be in [1, top_k = %d]", queries, per_query,
-                h->cfg.top_k);
-  if (h->pending[layer])
-    return fail(HISPARSE_ERR_STATE, "layer %d has a pending prefetch: join it with hisparse_resolve",
-                layer);
-  const int ke = queries * per_query;
-  if (int rc = check_no_overlap(h, sel, (size_t)h->cfg.num_requests * ke, ctx_len, out_slot))
-    return rc;
-  const ResolveShape sh = resolve_shape(h->cfg.top_k, h->cfg.cache_slots,
-                                        (h->cfg.flags & HISPARSE_DEBUG_VALIDATE) != 0, ke);
-  if (sh.lds_bytes > h->lds_max)
-    return fail(HISPARSE_ERR_UNSUPPORTED,
-                "C=%d with %d entries per request needs %zu bytes of LDS; the device has %zu",
-                h->cfg.cache_slots, ke, sh.lds_bytes, h->lds_max);
-  return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr, ke);
+  int rc = check_multi(h, sel, queries, per_query, ctx_len, layer, out_slot);
+  if (rc) return rc;
+  return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr, queries * per_query);
 }
 
 int hisparse_prefetch(hisparse_t h, hipStream_t main_stream, hipStream_t side_stream,
@@ -486,6 +494,27 @@ int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, con
     return hisparse_resolve(h, stream, sel, ctx_len, layer, out_slot);
   }
   return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr, 0,
+                         static_cast<const uint8_t*>(rows), pos);
+}
+
+int hisparse_append_resolve_multi(hisparse_t h, hipStream_t stream, int32_t layer,
+                                  const void* rows, const int32_t* pos, const int32_t* sel,
+                                  int32_t queries, int32_t per_query, const int32_t* ctx_len,
+                                  int32_t* out_slot) {
+  if (!h || !rows || !pos) return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  if (layer < 0 || layer >= h->cfg.num_layers)
+    return fail(HISPARSE_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (reinterpret_cast<uintptr_t>(rows) % 16 != 0)
+    return fail(HISPARSE_ERR_INVALID_ARG, "rows must be 16-byte aligned");
+  int rc = check_multi(h, sel, queries, per_query, ctx_len, layer, out_slot);
+  if (rc) return rc;  // nothing launched
+  if (h->cfg.resident_window == 0) {
+    // the appended position may be fetched by this resolve: append first
+    HIP_TRY(launch_append(h->view, stream, layer, static_cast<const uint8_t*>(rows), pos));
+    return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr,
+                           queries * per_query);
+  }
+  return enqueue_resolve(h, stream, sel, ctx_len, layer, out_slot, nullptr, queries * per_query,
                          static_cast<const uint8_t*>(rows), pos);
 }
 

@@ -267,6 +267,17 @@ int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, con
                             const int32_t* pos, const int32_t* sel, const int32_t* ctx_len,
                             int32_t* out_slot);
 
+/* hisparse_append followed by hisparse_resolve_multi on the same layer, in
+ * one launch when a resident window holds the appended position (two in
+ * order otherwise): the decode step of a growing context with several query
+ * tokens per request.  Arguments as for the two calls.  Errors: as
+ * hisparse_resolve_multi (checked before anything is launched), and
+ * INVALID_ARG for rows or pos. */
+int hisparse_append_resolve_multi(hisparse_t h, hipStream_t stream, int32_t layer,
+                                  const void* rows, const int32_t* pos, const int32_t* sel,
+                                  int32_t queries, int32_t per_query, const int32_t* ctx_len,
+                                  int32_t* out_slot);
+
 /* Return streams to the empty state (every slot free, clock 0).  layer and
  * request select one stream; -1 means all.  Used for admission and reuse of
  * a request slot.  Errors: INVALID_ARG, HIP. */

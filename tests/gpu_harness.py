@@ -144,17 +144,24 @@ class LockstepRun:
         self.oracle.append(s)
 
     def append_and_step(self, s: int):
-        """Step s of a growing workload through hisparse_append_resolve: every
-        layer's new row (s > 0) and its resolution in one call."""
+        """Step s of a growing workload through hisparse_append_resolve (or its
+        multi-query form): every layer's new row and its resolution in one
+        call."""
         cfg, torch = self.cfg, self.torch
-        assert self.queries == 1
         p = cfg.ctx_at(s) - 1
         for l in range(cfg.layers):
             rows = np.stack([appended_row(cfg, b, l, p) for b in range(cfg.B)])
             rows_dev = torch.from_numpy(rows).to(self.gpu.device)
-            hb.hisparse_append_resolve(self.gpu.h, self.gpu.stream, l, rows_dev.data_ptr(),
-                                       self.pos_dev[s].data_ptr(), self.sel_dev[s, l].data_ptr(),
-                                       self.ctx_dev[s].data_ptr(), self.out_dev[l].data_ptr())
+            if self.queries > 1:
+                hb.hisparse_append_resolve_multi(
+                    self.gpu.h, self.gpu.stream, l, rows_dev.data_ptr(), self.pos_dev[s].data_ptr(),
+                    self.sel_dev[s, l].data_ptr(), self.queries, cfg.k // self.queries,
+                    self.ctx_dev[s].data_ptr(), self.out_dev[l].data_ptr())
+            else:
+                hb.hisparse_append_resolve(self.gpu.h, self.gpu.stream, l, rows_dev.data_ptr(),
+                                           self.pos_dev[s].data_ptr(),
+                                           self.sel_dev[s, l].data_ptr(),
+                                           self.ctx_dev[s].data_ptr(), self.out_dev[l].data_ptr())
             torch.cuda.synchronize()
         self.oracle.append(s)
 

@@ -75,6 +75,31 @@ APPEND_CASES = {
 }
 
 
+@pytest.mark.parametrize("name,queries", [("window_37", 2), ("window_1", 3), ("no_window", 2),
+                                          ("pages_window", 2)])
+def test_append_resolve_multi_parity(name, queries):
+    """hisparse_append_resolve_multi equals the oracle's append followed by
+    its multi-query step."""
+    import torch
+    from tests.gpu_harness import LockstepRun
+    base, kw = APPEND_CASES[name]
+    cfg = WORKLOADS[base].scaled(**kw)
+    cfg = cfg.scaled(k=(cfg.k // queries) * queries)
+    print(f"[append_resolve_multi] {name} Q={queries}: k={cfg.k}", flush=True)
+    run = LockstepRun(cfg, queries=queries)
+    try:
+        for s in range(cfg.steps):
+            if s > 0:
+                run.append_and_step(s)
+            else:
+                run.gpu_step(s)
+            torch.cuda.synchronize()
+            run.compare_step(s, run.oracle_step(s))
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+
+
 @pytest.mark.parametrize("flags", ["none", "no_io"])
 @pytest.mark.parametrize("mode", ["fused", "split"])
 @pytest.mark.parametrize("name", sorted(APPEND_CASES))
