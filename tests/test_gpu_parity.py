@@ -182,3 +182,27 @@ def test_hand_examples_on_gpu(golden):
         assert g.status() == 0
     finally:
         g.close()
+
+
+def test_long_run_many_cache_turnovers():
+    """400 steps on small caches (the LRU order, stamps and the position map
+    turn over dozens of times), compared with the oracle every step; full
+    state and slot bytes every 50 steps."""
+    import torch
+    from tests.gpu_harness import LockstepRun
+    cfg = WORKLOADS[2].scaled(B=2, L0=20000, C=1200, R=16, k=600, steps=400, carry_pct=60)
+    print(f"[long run] {cfg.steps} steps, C={cfg.C}, k={cfg.k}", flush=True)
+    run = LockstepRun(cfg)
+    try:
+        for s in range(cfg.steps):
+            run.gpu_step(s)
+            torch.cuda.synchronize()
+            full = s % 50 == 49
+            run.compare_step(s, run.oracle_step(s), full_state=full, contents=full)
+            if full:
+                print(f"[long run] step {s + 1} matches", flush=True)
+        assert run.gpu.status() == 0
+        hdr = run.gpu.hdr(0, 0)
+        assert int(hdr[0]) == cfg.steps
+    finally:
+        run.close()
