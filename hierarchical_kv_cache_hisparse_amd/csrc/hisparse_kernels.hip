@@ -26,9 +26,16 @@
 //     stamp, so the next order is "unreferenced, not evicted, in old order"
 //     followed by "referenced or refilled, by slot number"; the victims are
 //     the first M unreferenced entries of the old order.  O(C) per step;
-//   * the miss fetch is a separate launch fanned out over the whole chip:
-//     16-byte non-temporal loads straight from mapped host memory, written to
-//     the slot rows in HBM.  No MFMA anywhere: nothing here is a contraction.
+//   * the miss fetch: 16-byte non-temporal loads straight from mapped host
+//     memory (through the global address space, so they count in vmcnt
+//     only), written to the slot rows in HBM.  With >= 8 streams per call the
+//     resolve workgroups copy their own misses (the first chunks are
+//     requested before the victims are chosen); with fewer, a separate launch
+//     fans the copies out over ~64 workgroups;
+//   * the new row of a growing context can be appended in the same launch
+//     (a separate instantiation), since with a resident window it is never
+//     looked up or fetched by the resolution.
+//   No MFMA anywhere: nothing here is a contraction.
 #include <hip/hip_runtime.h>
 
 #include "hisparse_device.h"
