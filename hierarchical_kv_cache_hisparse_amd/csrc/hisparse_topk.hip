@@ -22,13 +22,15 @@
 //      grid shape, so the same XCD and, mostly, its L2), sets the bits of
 //      the positions above that bin in a per-row bitmap and appends the
 //      positions inside it to a candidate list (one global counter update
-//      per workgroup);
-//   3. finish (one workgroup of 1024 threads per row): a radix select with
-//      12-bit digits over the candidates' remaining key bits and inverted
-//      position, staged in LDS and stopped as soon as a whole digit bin is
-//      taken, picks exactly the missing count; then the bitmap becomes the
-//      ascending position list through one block scan of per-thread
-//      popcounts.
+//      per workgroup), counting them by the next 12 key bits (the level-2
+//      histogram);
+//   3. finish (one workgroup of 1024 threads per row): one crossing search
+//      over the level-2 histogram; a level-2 bin needed whole is taken
+//      whole, else its candidates (at most 512) rank themselves by direct
+//      counting over (remaining key bits, inverted position), and larger
+//      ties fall back to a radix select over those bits; marks go to an LDS
+//      copy of the bitmap, which becomes the ascending position list through
+//      one block scan of per-thread popcounts.
 // The histogram and the candidate counter are zero on entry and zeroed again
 // by the finish kernel, so the three launches capture into a HIP graph with
 // no memset nodes and replay any number of times.
