@@ -387,6 +387,11 @@ int hisparse_create(const hisparse_config* cfg, void* const* host_rows, void* de
   if (mode && !strcmp(mode, "fused")) v.fuse_fetch = 1;
   else if (mode && !strcmp(mode, "split")) v.fuse_fetch = 0;
   else v.fuse_fetch = B >= 8 ? 1 : 0;
+  // The fetch kernel indexes a layer call's chunks (B * k * row_bytes/16 at
+  // most) with 32-bit counters and rounds the count up to a multiple of its
+  // grid; past 2^31 chunks only the fused copy (per-stream counts) is used.
+  if (!v.fuse_fetch && (int64_t)B * cfg->top_k * (cfg->row_bytes / 16) >= (int64_t(1) << 31))
+    v.fuse_fetch = 1;
   const int wgs = env_int("HISPARSE_FETCH_WORKGROUPS", 64);
   h->fetch_grid_x = wgs > 1 ? wgs : 1;
 
