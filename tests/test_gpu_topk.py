@@ -2,7 +2,8 @@
 topk_select, bit-exact per row: seeded drifting N(0,1) scores with and
 without bfloat16 ties and special values, ragged lengths, per-row context
 lengths, all-equal rows (every position a boundary candidate), the full
-per-layer shapes of the token and page workloads, workspace reuse, graph
+per-layer shapes of the token and page workloads, rows on both sides of the
+finish kernel's 2^18-position LDS bitmap limit, workspace reuse, graph
 replay, and the selection fed straight into the resolver."""
 import numpy as np
 import pytest
@@ -59,6 +60,10 @@ CASES = {
     "k_one": (2, 70000, 1, None, {"ties": True}),
     "k_max": (2, 30000, 4096, [30000, 4100], {"ties": True, "specials": True}),
     "one_chunk": (3, 4096, 64, None, {}),
+    # the longest rows whose bitmap the finish kernel keeps in LDS (2^18)
+    "overlay_max_len": (2, 262144, 1000, [262144, 262143], {"specials": True}),
+    # longer rows: the finish kernel marks and reads the global bitmap
+    "long_rows": (3, 300001, 2048, [300001, 270000, 5000], {"ties": True}),
 }
 
 
