@@ -10,10 +10,12 @@ host memory, which is where the method keeps them.
 
 Prints one JSON line.  ``value`` is resolved top-k entries per second over
 the timed region: all K steps captured as one HIP graph (as a decode graph
-holds them) and replayed once from a cold cache.  The dominant kernel's
-roofline uses HIP-event kernel durations from an eager pass over the same K
-steps (events cannot be recorded inside a graph), whose throughput is
-reported too.  Also reported: miss-fetch GB/s against the host link
+holds them) and replayed once from a cold cache.  When each layer call is one
+launch (the fused copy), the dominant kernel's average launch duration comes
+from HIP events on the launch stream around that timed replay; otherwise
+(separate fetch launches, which events cannot split inside a graph) from an
+eager pass over the same K steps with the library's HIP events around each
+launch, whose throughput is reported too.  Also reported: miss-fetch GB/s against the host link
 (theoretical PCIe Gen5 x16 and the measured peak of this machine), the resolve
 kernel against HBM, the no-IO (copies suppressed) per-layer call time under
 graph replay, and the CPU oracle timed on the host's cores.
@@ -55,6 +57,9 @@ def parse_args():
                          "(metadata only), for profiling the resolve kernel alone")
     ap.add_argument("--only-timed", action="store_true",
                     help="only the eager timed region (for profiler runs)")
+    ap.add_argument("--with-graph", action="store_true",
+                    help="with --only-timed: also the timed graph replay (for profiler runs "
+                         "of the launches the roofline times)")
     ap.add_argument("--host-noncoherent", action="store_true",
                     help="allocate host histories non-coherent (GPU-cacheable)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -86,6 +91,8 @@ def parse_args():
                     help="summarize rocprofv3 CSV output in DIR into profiles/ and exit")
     ap.add_argument("--label", help="summary name (with --summarize-rocprof)")
     ap.add_argument("--command", help="the profiled command line (with --summarize-rocprof)")
+    ap.add_argument("--trace-tail", type=int, default=0,
+                    help="with --summarize-rocprof: also the mean over each kernel's last N launches")
     return ap.parse_args()
 
 
@@ -309,9 +316,11 @@ def short_kernel_name(name):
     return name.split("(")[0][-48:]
 
 
-def summarize_rocprof(directory, label, command):
+def summarize_rocprof(directory, label, command, tail=0):
     """Turn rocprofv3 CSV output (kernel trace + stats, or one PMC counter)
-    into a short Markdown summary under profiles/."""
+    into a short Markdown summary under profiles/.  With tail > 0 the trace
+    table also gives each kernel's mean over its last `tail` launches (in
+    start order), e.g. the launches of the timed graph replay."""
     import csv
     import glob
     lines = [f"# {label}", "", f"Command: `{command}`", ""]
@@ -334,14 +343,22 @@ def summarize_rocprof(directory, label, command):
         import statistics
         per = {}
         with open(trace[0]) as f:
-            for row in csv.DictReader(f):
-                d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
-                per.setdefault(short_kernel_name(row["Kernel_Name"]), []).append(d)
-        lines += ["## kernel trace: per-launch durations (us)", "",
-                  "| kernel | launches | mean | median | first launch |", "|---|---|---|---|---|"]
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+        for row in rows:
+            d = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            per.setdefault(short_kernel_name(row["Kernel_Name"]), []).append(d)
+        head = "| kernel | launches | mean | median | first launch |"
+        rule = "|---|---|---|---|---|"
+        if tail:
+            head += f" mean of the last {tail} |"
+            rule += "---|"
+        lines += ["## kernel trace: per-launch durations (us)", "", head, rule]
         for k, v in per.items():
-            lines.append(f"| {k} | {len(v)} | {statistics.mean(v):.3f} | "
-                         f"{statistics.median(v):.3f} | {v[0]:.3f} |")
+            line = (f"| {k} | {len(v)} | {statistics.mean(v):.3f} | "
+                    f"{statistics.median(v):.3f} | {v[0]:.3f} |")
+            if tail:
+                line += f" {statistics.mean(v[-tail:]):.3f} |" if len(v) >= tail else " - |"
+            lines.append(line)
         lines.append("")
     if pmc:
         agg = {}
@@ -839,7 +856,8 @@ def cpu_model():
 def main():
     args = parse_args()
     if args.summarize_rocprof:
-        summarize_rocprof(args.summarize_rocprof, args.label or "profile", args.command or "")
+        summarize_rocprof(args.summarize_rocprof, args.label or "profile", args.command or "",
+                          tail=args.trace_tail)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the resolve path has no cross-GPU step, and this "
@@ -919,7 +937,8 @@ def main():
         # ---- the timed region: all K steps (every layer's call) captured as
         # one HIP graph, as a decode graph holds them, replayed once from a
         # cold cache after one warm replay ------------------------------------
-        if args.only_timed:
+        graph_ev_ms = None
+        if args.only_timed and not args.with_graph:
             elapsed = elapsed_eager
             mode = "eager, library HIP-event timing on"
         else:
@@ -927,10 +946,17 @@ def main():
             graph.replay()
             torch.cuda.synchronize()
             setup.reset(io)
+            # HIP events on the stream the graph is launched on, around the
+            # timed replay: its nodes are the K steps' resolve launches
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
             t0 = time.perf_counter()
+            ev0.record()
             graph.replay()
+            ev1.record()
             torch.cuda.synchronize()
             elapsed = time.perf_counter() - t0
+            graph_ev_ms = ev0.elapsed_time(ev1)
             assert io.status() == 0, "device status word set during the benchmark"
             assert tuple(int(x) for x in setup.totals(io)) == (tot_miss, tot_evict, tot_hit), \
                 "graph replay and eager pass disagree"
@@ -944,9 +970,17 @@ def main():
 
         fused = timing["fetch_launches"] == 0
         resolve_avg_s = timing["resolve_ms"] / max(1, timing["resolve_launches"]) / 1e3
+        # one launch per layer call (the resolve kernel, with the append fused
+        # in when the context grows): then the timed graph holds nothing else
+        one_launch = fused and (not cfg.growth or cfg.R > 0)
+        launch_timing = "eager pass, library HIP events around each launch"
         if fused:   # the resolve workgroups copy their own misses
             fetch_avg_s = resolve_avg_s
             fetch_bytes_per_launch = miss_bytes / max(1, timing["resolve_launches"])
+            if one_launch and graph_ev_ms is not None:
+                fetch_avg_s = graph_ev_ms / 1e3 / (K * cfg.layers)
+                launch_timing = ("timed region: HIP events on the launch stream around the graph "
+                                 "replay, whose K x layers nodes are the resolve launches")
         else:
             fetch_avg_s = timing["fetch_ms"] / max(1, timing["fetch_launches"]) / 1e3
             fetch_bytes_per_launch = miss_bytes / max(1, timing["fetch_launches"])
@@ -987,7 +1021,11 @@ def main():
                          "traffic_read_bytes": round(traffic["FETCH_SIZE"]) if traffic else None,
                          "traffic_write_bytes": round(traffic["WRITE_SIZE"]) if traffic else None,
                          "per_launch_bytes": round(fetch_bytes_per_launch),
-                         "avg_launch_us": round(fetch_avg_s * 1e6, 3)},
+                         "avg_launch_us": round(fetch_avg_s * 1e6, 3),
+                         "launch_timing": launch_timing,
+                         "avg_launch_us_eager": round(
+                             (resolve_avg_s if fused else
+                              timing["fetch_ms"] / max(1, timing["fetch_launches"]) / 1e3) * 1e6, 3)},
             "resolve_kernel": {"bound": "hbm", "per_launch_bytes": round(meta_bytes),
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                "note": "metadata only: the kernel timed on the instance "
