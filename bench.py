@@ -1057,23 +1057,30 @@ def main():
         if not args.only_timed:
             # ---- graph replay, best of 3 (IO and no-IO) --------------------
             def graph_pass(inst):
-                """All K steps in one HIP graph, replayed from a cold cache."""
+                """All K steps in one HIP graph, replayed from a cold cache:
+                best wall time and best HIP-event time (ms) of 3 replays."""
                 g = capture_steps(setup, inst, K)
                 g.replay()                      # warm replay
                 torch.cuda.synchronize()
-                best = None
+                best, best_ev = None, None
                 for _ in range(3):
                     setup.reset(inst)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
                     t0 = time.perf_counter()
+                    e0.record()
                     g.replay()
+                    e1.record()
                     torch.cuda.synchronize()
                     dt = time.perf_counter() - t0
                     best = dt if best is None else min(best, dt)
+                    ev = e0.elapsed_time(e1)
+                    best_ev = ev if best_ev is None else min(best_ev, ev)
                 assert inst.status() == 0
-                return best
+                return best, best_ev
 
-            dt_io = graph_pass(io)
-            dt_noio = graph_pass(setup.noio)
+            dt_io, _ = graph_pass(io)
+            dt_noio, ev_noio_ms = graph_pass(setup.noio)
             # resolve kernel alone, copies suppressed: eager launches, HIP events
             setup.reset(setup.noio)
             hb.hisparse_set_timing(setup.noio.h, True)
@@ -1083,8 +1090,19 @@ def main():
             hb.hisparse_set_timing(setup.noio.h, False)
             noio_kernel_us = t_noio["resolve_ms"] / max(1, t_noio["resolve_launches"]) * 1e3
             rk = result["resolve_kernel"]
-            rk["avg_launch_us"] = round(noio_kernel_us, 3)
-            rk["achieved"] = round(meta_bytes / (noio_kernel_us * 1e-6) / 1e9, 3)
+            # copies suppressed, every layer call is one launch (the append is
+            # fused in when the context grows and a window exists): the graph's
+            # nodes are the K x layers resolve launches
+            if not cfg.growth or cfg.R > 0:
+                rk_us = ev_noio_ms * 1e3 / (K * cfg.layers)
+                rk["launch_timing"] = ("HIP events around the copy-free graph replay (best of 3), "
+                                       "whose K x layers nodes are the resolve launches")
+            else:
+                rk_us = noio_kernel_us
+                rk["launch_timing"] = "eager pass, library HIP events around each launch"
+            rk["avg_launch_us"] = round(rk_us, 3)
+            rk["avg_launch_us_eager"] = round(noio_kernel_us, 3)
+            rk["achieved"] = round(meta_bytes / (rk_us * 1e-6) / 1e9, 3)
             rk["frac"] = round(rk["achieved"] / HBM_PEAK_GBPS, 6)
             t_meta = committed_traffic("resolve_kernel", cfg.label, "noio")
             rk["traffic"] = round(t_meta["FETCH_SIZE"] + t_meta["WRITE_SIZE"]) if t_meta else None
