@@ -38,6 +38,9 @@ CASES = {
     "k_one": (2, dict(B=2, L0=500, C=4, R=3, k=1, steps=20, carry_pct=0)),
     "largest_supported_shape": (1, dict(L0=60000, C=12000, k=3000, steps=4)),
     "window_covers_context": (3, dict(B=2, layers=1, L0=40, C=64, R=64, k=32, steps=12)),
+    # the context grows past the window (58 .. 69 rows, R = 64): the first steps are all
+    # resident, then the oldest positions leave the window and are fetched when selected
+    "window_boundary_crossing": (3, dict(B=2, layers=1, L0=58, C=64, R=64, k=24, steps=12)),
 }
 
 
