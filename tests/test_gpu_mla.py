@@ -99,6 +99,37 @@ def test_attention_over_token_slots(H):
     _run(cfg, H)
 
 
+@pytest.mark.parametrize("fused_append", [True, False])
+def test_attention_over_a_growing_context(fused_append):
+    """Independent per-layer selections over a context that grows by one row
+    per step: the newest row reaches its ring slot through the append (fused
+    into the resolve launch, or a separate append launch) and is attended
+    from there, the oldest leaves the window; every step's attention equals
+    the oracle over the host rows."""
+    import torch
+    from tests.gpu_harness import LockstepRun
+    cfg = WORKLOADS[3].scaled(B=3, layers=2, L0=6000, C=1200, R=37, k=500, steps=5)
+    run = LockstepRun(cfg, oracle_streams=[])
+    attn = Attn(run, 16)
+    worst = 0.0
+    try:
+        for s in range(cfg.steps):
+            if s > 0 and fused_append:
+                run.append_and_step(s)
+            else:
+                if s > 0:
+                    run.append_rows(s)
+                run.gpu_step(s)
+            for l in range(cfg.layers):
+                attn.launch(l, run.out_dev[l])
+                torch.cuda.synchronize()
+                worst = max(worst, attn.check(s, l))
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+    print(f"[mla] growing context, max |out - oracle| = {worst:.3e}")
+
+
 def test_attention_over_page_slots():
     cfg = WORKLOADS[5].scaled(B=2, layers=2, L0=3000, C=64, k=40, steps=3)
     _run(cfg, 16)
