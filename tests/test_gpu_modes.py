@@ -169,6 +169,71 @@ def test_prefetch_equals_no_prefetch(captured):
         a.close()
 
 
+def test_prefetch_with_a_growing_context():
+    """Shared selections over a context that grows by one row per step: each
+    layer's new row goes in through hisparse_append_resolve while the layer
+    after it has been prefetched on a second stream (the append then runs as
+    its own launch before the join).  Slot maps, state, slot bytes and the
+    resident ring equal appending and resolving every layer in order."""
+    torch, hb = _torch(), _hb()
+    from tests.harness import appended_row
+    cfg = WORKLOADS[4].scaled(B=2, layers=3, L0=20000, growth=1, steps=6)
+    a, b, trace = _pair(cfg)
+    try:
+        dev = "cuda:0"
+        ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device=dev)
+        _load_windows(a, ctx)
+        _load_windows(b, ctx)
+        trace_dev = torch.from_numpy(trace).to(dev)
+        sel_buf = torch.empty((cfg.B, cfg.k), dtype=torch.int32, device=dev)
+        pos_buf = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
+        rows_dev = torch.empty((cfg.layers, cfg.B, cfg.row_bytes), dtype=torch.uint8, device=dev)
+        out_p = torch.empty((cfg.layers, cfg.B, cfg.k), dtype=torch.int32, device=dev)
+        out_s = torch.empty_like(out_p)
+        main = torch.cuda.Stream()
+        side = torch.cuda.Stream()
+
+        def layer_call(inst, st, l, grow, out):
+            if grow:
+                hb.hisparse_append_resolve(inst.h, st, l, rows_dev[l].data_ptr(),
+                                           pos_buf.data_ptr(), sel_buf.data_ptr(),
+                                           ctx.data_ptr(), out[l].data_ptr())
+            else:
+                hb.hisparse_resolve(inst.h, st, sel_buf.data_ptr(), ctx.data_ptr(), l,
+                                    out[l].data_ptr())
+
+        for step in range(cfg.steps):
+            c = cfg.ctx_at(step)
+            grow = step > 0
+            ctx.fill_(c)
+            pos_buf.fill_(c - 1)
+            sel_buf.copy_(trace_dev[step, 0])
+            rows_dev.copy_(torch.from_numpy(np.stack([
+                np.stack([appended_row(cfg, bb, l, c - 1) for bb in range(cfg.B)])
+                for l in range(cfg.layers)])))
+            torch.cuda.synchronize()
+            with torch.cuda.stream(main):
+                ms, ss = main.cuda_stream, side.cuda_stream
+                layer_call(a, ms, 0, grow, out_p)
+                for l in range(cfg.layers - 1):
+                    hb.hisparse_prefetch(a.h, ms, ss, sel_buf.data_ptr(), ctx.data_ptr(), l + 1)
+                    layer_call(a, ms, l + 1, grow, out_p)
+            torch.cuda.synchronize()
+            for l in range(cfg.layers):
+                layer_call(b, b.stream, l, grow, out_s)
+            torch.cuda.synchronize()
+            assert torch.equal(out_p, out_s), f"step {step}"
+            _assert_same_state(a, b, cfg)
+            for l in range(cfg.layers):
+                for bb in range(cfg.B):
+                    np.testing.assert_array_equal(a.slots(bb, l)[cfg.C:], b.slots(bb, l)[cfg.C:],
+                                                  err_msg=f"ring step {step} b={bb} l={l}")
+        assert a.status() == 0 and b.status() == 0
+    finally:
+        b.close()
+        a.close()
+
+
 def test_prefetch_misuse_is_reported():
     torch, hb = _torch(), _hb()
     cfg = WORKLOADS[4].scaled(B=2, layers=2, L0=5000, steps=2)
