@@ -993,6 +993,7 @@ def main():
         avg_hit = tot_hit / max(1, n_calls * cfg.B)
         meta_bytes = cfg.B * (12 * cfg.k + 16 * cfg.C + 4 * (avg_hit + avg_miss) + 24 * avg_miss + 64)
         dominant = "resolve_kernel" if fused else "fetch_kernel"
+        alg_traffic = 2 * fetch_bytes_per_launch + (meta_bytes if fused else 0)
         traffic = committed_traffic(dominant, cfg.label, "fused" if fused else "split")
 
         result = {
@@ -1021,6 +1022,12 @@ def main():
                          "traffic_read_bytes": round(traffic["FETCH_SIZE"]) if traffic else None,
                          "traffic_write_bytes": round(traffic["WRITE_SIZE"]) if traffic else None,
                          "per_launch_bytes": round(fetch_bytes_per_launch),
+                         # what `traffic` counts, algorithmically: the missed rows read
+                         # over the link and written to HBM, plus (fused) the metadata
+                         "algorithmic_traffic_bytes": round(alg_traffic),
+                         "traffic_over_algorithmic": (
+                             round((traffic["FETCH_SIZE"] + traffic["WRITE_SIZE"]) / alg_traffic, 3)
+                             if traffic else None),
                          "avg_launch_us": round(fetch_avg_s * 1e6, 3),
                          "launch_timing": launch_timing,
                          "avg_launch_us_eager": round(
