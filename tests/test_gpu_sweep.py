@@ -13,7 +13,7 @@ import pytest
 
 from workload import WORKLOADS
 
-N_CASES = 24
+N_CASES = 120
 # C for each items-per-thread shape: max(k, C) <= 1024 x items
 C_FOR_IPT = {1: 700, 2: 1500, 3: 2500, 4: 3900, 6: 5000, 8: 7000, 12: 10000, 16: 15000}
 
