@@ -280,3 +280,28 @@ def test_attention_multi_with_one_token_is_the_single_call():
             assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
     finally:
         run.close()
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_attention_random_shapes(i):
+    """Seeded random shapes over real slot maps: token rows or 16-token pages,
+    1-4 requests, 16-128 heads, any selection width up to the cache, with and
+    without a resident window."""
+    rng = np.random.default_rng(9500 + i)
+    pages = rng.random() < 0.3
+    B = int(rng.integers(1, 5))
+    H = int(rng.choice([16, 32, 48, 64, 128]))
+    if pages:
+        C = int(rng.integers(8, 300))
+        k = int(rng.integers(1, min(C, 128) + 1))
+        L0 = int(rng.integers(4 * k + 40, 4 * k + 2000))
+        R = int(rng.choice([0, 1, 4]))
+        cfg = WORKLOADS[5].scaled(B=B, layers=1, L0=L0, C=C, R=R, k=k, steps=2)
+    else:
+        C = int(rng.integers(16, 5000))
+        k = int(rng.integers(1, min(C, 4096) + 1))
+        R = int(rng.choice([0, 1, 37, 128]))
+        L0 = int(rng.integers(4 * k + R + 64, 4 * k + R + 20000))
+        cfg = WORKLOADS[2].scaled(B=B, layers=1, L0=L0, C=C, R=R, k=k, steps=2)
+    print(f"[mla random {i}] pages={pages} B={B} H={H} C={C} k={k} R={R} L0={L0}", flush=True)
+    _run(cfg, H)

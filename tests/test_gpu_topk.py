@@ -192,3 +192,33 @@ def test_topk_argument_checks():
                              kw["num_rows"], kw["max_len"], t.ctx.data_ptr(), kw["k"],
                              t.ws.data_ptr(), out.data_ptr())
         assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG, b
+
+
+def _random_topk_case(i):
+    """Seeded random shape: rows, row length (short, mid, or past the finish
+    kernel's 2^18-position LDS bitmap), k, ragged per-row contexts, bf16 ties,
+    special values and plateaus of equal scores.  Pure function of i."""
+    from workload.scores import score_rows
+    rng = np.random.default_rng(9000 + i)
+    rows = int(rng.integers(1, 9))
+    n = int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(5000, 70000)),
+                        int(rng.integers(250000, 300000))]))
+    k = int(rng.integers(1, 4097))
+    ctx = [int(rng.choice([n, int(rng.integers(0, n + 1)), min(n, k), max(0, k - 1)]))
+           for _ in range(rows)]
+    kw = [{}, {"ties": True}, {"specials": True}, {"ties": True, "specials": True}][
+        int(rng.integers(0, 4))]
+    sc = score_rows(rows, n, 9100 + i, 0, 0, **kw)
+    if rng.random() < 0.15:
+        a = int(rng.integers(0, n))
+        b = int(rng.integers(a, n + 1))
+        sc[:, a:b] = np.float32(rng.choice([0.0, -0.0, 1.5, np.inf, -np.inf]))
+    return rows, n, k, ctx, sc
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_topk_random_shapes(i):
+    rows, n, k, ctx, sc = _random_topk_case(i)
+    print(f"[topk random {i}] rows={rows} n={n} k={k} ctx={ctx}", flush=True)
+    t = Topk(rows, n)
+    _check(t.run(sc, ctx, k), sc, ctx, k, f"random case {i}")
