@@ -5,7 +5,8 @@ counters, LRU state, eviction logs, slot bytes).
 The draws cover every items-per-thread shape of the resolve kernel (the
 cache size C picks it: 1, 2, 3, 4, 6, 8, 12 and 16 items per thread, with
 and without the early host reads of the fused copy), every structure of the
-five workloads (one request, a resident window, growth by appends, shared
+five workloads (one request, a resident window, growth by appends -- fused
+into the resolve call in even cases, a separate launch in odd ones -- shared
 selections, 18 KiB page rows), both miss-fetch paths, the copy-free and
 duplicate-checking flags, and several query tokens per request."""
 import numpy as np
@@ -91,9 +92,12 @@ def test_random_case_parity(i, monkeypatch):
     run = LockstepRun(cfg, flags=fl, queries=queries)
     try:
         for s in range(cfg.steps):
-            if s > 0 and cfg.growth:
-                run.append_rows(s)
-            run.gpu_step(s)
+            if s > 0 and cfg.growth and i % 2 == 0:
+                run.append_and_step(s)         # append fused into the resolve call
+            else:
+                if s > 0 and cfg.growth:
+                    run.append_rows(s)         # separate append launch
+                run.gpu_step(s)
             torch.cuda.synchronize()
             run.compare_step(s, run.oracle_step(s), full_state=(s == cfg.steps - 1),
                              contents=(s == cfg.steps - 1))
