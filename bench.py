@@ -1015,6 +1015,10 @@ def main():
                        "carry_over_pct": cfg.carry_pct, "replacement": cfg.replacement,
                        "timed_launch_mode": mode},
             "roofline": {"bound": "host_link", "kernel": dominant, "fused_fetch": fused,
+                         "bound_note": "the miss fetch moves missed rows from pinned host memory "
+                                       "over PCIe Gen5 x16; it is bound by that link, not by HBM "
+                                       "(see traffic) or MFMA (none is used): peak = the link's "
+                                       "64 GB/s, peak_measured = this host's measured H2D peak",
                          "achieved": round(fetch_gbps, 3), "peak": LINK_PEAK_THEORETICAL_GBPS,
                          "unit": "GB/s", "frac": round(fetch_gbps / LINK_PEAK_THEORETICAL_GBPS, 4),
                          "traffic": (round(traffic["FETCH_SIZE"] + traffic["WRITE_SIZE"])
