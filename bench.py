@@ -47,9 +47,18 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: the workload's own step count, 64 for workload 2)")
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", type=int, default=2,
-                    help="workload 1..5 of workload/configs.py (default 2: 8 requests, 1 layer, "
-                         "131072 token rows)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="workload 1..5 of workload/configs.py (default 4: 16 requests x 8 layers "
+                         "sharing one selection, 262144 token rows, the next layer prefetched on "
+                         "a second stream; the largest workload of the five)")
+    ap.add_argument("--serial", action="store_true",
+                    help="shared-selection workloads: resolve every layer on the main stream "
+                         "instead of the workload's layer-wise prefetch schedule")
+    ap.add_argument("--no-prefetch-study", action="store_true",
+                    help="skip the prefetch hidden-fraction study of the default run")
+    ap.add_argument("--numa-node", type=int, default=-1,
+                    help="NUMA node of the pinned host histories (-1: the GPU's own node, "
+                         "-2: the process's default policy)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip the link-peak probe")
     ap.add_argument("--no-io", action="store_true",
@@ -115,12 +124,15 @@ def host_mem_available_gib():
 class Setup:
     """Host histories, two library instances (IO and no-IO) and device inputs."""
 
-    def __init__(self, cfg, host_flags, queries=1):
+    def __init__(self, cfg, host_flags, queries=1, numa_node=-1, prefetch=False):
         import torch
         from hierarchical_kv_cache_hisparse_amd import binding as hb
-        from tests.gpu_harness import GpuInstance, host_view
-        from tests.harness import appended_row, fill_host, make_trace
+        from hierarchical_kv_cache_hisparse_amd.instance import GpuInstance, host_view
+        from workload.prepare import appended_row, fill_host, make_trace
         self.torch, self.hb, self.cfg, self.queries = torch, hb, cfg, queries
+        # the workload's layer-wise prefetch schedule (shared selections only)
+        self.prefetch = bool(prefetch and cfg.shared_selection and cfg.layers > 1 and queries == 1)
+        self.side = torch.cuda.Stream() if self.prefetch else None
         t0 = time.time()
         self.trace = make_trace(cfg, queries=queries)                  # [S, L, B, k]
         nbytes = cfg.l_cap * cfg.row_bytes
@@ -130,11 +142,23 @@ class Setup:
         self.hosts = {}
         for l in range(cfg.layers):
             for b in range(cfg.B):
-                ptr = hb.hisparse_host_alloc(nbytes, host_flags)
+                ptr = hb.hisparse_host_alloc(nbytes, host_flags, numa_node)
                 self.hosts[(b, l)] = (ptr, host_view(ptr, nbytes).reshape(cfg.l_cap, cfg.row_bytes))
         streams = list(self.hosts)
         fill_host(cfg, lambda b, l: self.hosts[(b, l)][1], self.trace, streams)
-        log(f"host histories: {len(streams)} x {nbytes / 2**20:.1f} MiB pinned, filled in "
+        # where the histories landed: the node of a few touched pages of the
+        # first and last history, next to the GPU's own node
+        self.host_memory["numa_node_requested"] = numa_node
+        self.host_memory["gpu_numa_node"] = hb.hisparse_device_numa_node()
+        nodes = set()
+        for key in (streams[0], streams[-1]):
+            ptr, view = self.hosts[key]
+            for frac in (0.0, 0.5, 0.999):
+                row = int(frac * (cfg.l_cap - 1))
+                nodes.add(hb.hisparse_host_numa_node(ptr + row * cfg.row_bytes))
+        self.host_memory["history_numa_nodes"] = sorted(nodes)
+        log(f"host histories: {len(streams)} x {nbytes / 2**20:.1f} MiB pinned on NUMA node(s) "
+            f"{sorted(nodes)} (GPU node {self.host_memory['gpu_numa_node']}), filled in "
             f"{time.time() - t0:.1f}s")
         self.io = GpuInstance(cfg, flags=0, hosts=self.hosts)
         self.noio = GpuInstance(cfg, flags=hb.HISPARSE_NO_IO, hosts=self.hosts)
@@ -165,6 +189,19 @@ class Setup:
     def step(self, inst, s, stream=None):
         hb, cfg = self.hb, self.cfg
         st = self.torch.cuda.current_stream().cuda_stream if stream is None else stream
+        if self.prefetch:
+            # shared selections: layer 0 on the main stream; every layer l+1
+            # prefetched on the side stream (forked after layer l's call) and
+            # joined by its resolve
+            ctx = self.ctx[s].data_ptr()
+            hb.hisparse_resolve(inst.h, st, self.sel[s, 0].data_ptr(), ctx, 0,
+                                self.out[0].data_ptr())
+            for l in range(cfg.layers - 1):
+                hb.hisparse_prefetch(inst.h, st, self.side.cuda_stream,
+                                     self.sel[s, l + 1].data_ptr(), ctx, l + 1)
+                hb.hisparse_resolve(inst.h, st, self.sel[s, l + 1].data_ptr(), ctx, l + 1,
+                                    self.out[l + 1].data_ptr())
+            return
         for l in range(cfg.layers):
             if cfg.growth and s > 0:
                 # the decode step of a growing context: append + resolve, one call
@@ -188,15 +225,7 @@ class Setup:
 
     def totals(self, inst):
         """Summed running counters of every stream (misses, evictions, hits)."""
-        hb = self.hb
-        tot = np.zeros(3, np.int64)
-        for l in range(self.cfg.layers):
-            for b in range(self.cfg.B):
-                h = inst.hdr(b, l)
-                tot += h[[hb.HDR_TOTAL_MISS, hb.HDR_TOTAL_EVICT, hb.HDR_TOTAL_HIT]].astype(np.int64) + \
-                    (h[[hb.HDR_TOTAL_MISS + 1, hb.HDR_TOTAL_EVICT + 1, hb.HDR_TOTAL_HIT + 1]]
-                     .astype(np.int64) << 32)
-        return tot
+        return inst.totals()
 
     def close(self):
         self.io.close()
@@ -205,40 +234,46 @@ class Setup:
             self.hb.hisparse_host_free(ptr)
 
 
-def link_probe(torch, hb):
-    """Host->device peak of this machine: hipMemcpyAsync of 256 MiB from pinned
-    memory, and a zero-copy 16-byte-load kernel over 256 MiB; best of 5."""
+def link_probe(torch, hb, numa_node=-1):
+    """Host->device peak of this machine, from pinned memory on the histories'
+    NUMA node: hipMemcpyAsync of 256 MiB (through torch's copy), and a
+    zero-copy 16-byte-load kernel over 256 MiB at several grid sizes; best
+    of 5 each.  torch's own pinned allocator is measured too, for context."""
+    from hierarchical_kv_cache_hisparse_amd.instance import host_view
     nbytes = 256 << 20
     dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
-    pinned = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-    pinned.fill_(1)
+
+    def best_of(fn, n=5):
+        best = 0.0
+        for _ in range(n):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (time.perf_counter() - t0) / 1e9)
+        return round(best, 2)
+
     res = {}
-    best = 0.0
-    for _ in range(5):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        dev.copy_(pinned, non_blocking=True)
-        torch.cuda.synchronize()
-        best = max(best, nbytes / (time.perf_counter() - t0) / 1e9)
-    res["memcpy_h2d_GBps"] = round(best, 2)
-    ptr = hb.hisparse_host_alloc(nbytes, hb.HISPARSE_HOST_COHERENT)
+    ptr = hb.hisparse_host_alloc(nbytes, hb.HISPARSE_HOST_COHERENT, numa_node)
     try:
-        from tests.gpu_harness import host_view
-        host_view(ptr, nbytes)[:] = 1
+        view = host_view(ptr, nbytes)
+        view[:] = 1
+        res["numa_node"] = hb.hisparse_host_numa_node(ptr)
+        src = torch.from_numpy(view)   # the pinned allocation, as a CPU tensor
+        res["memcpy_h2d_GBps"] = best_of(lambda: dev.copy_(src, non_blocking=True))
         stream = torch.cuda.current_stream().cuda_stream
         per_wg = {}
         for wgs in (1, 4, 8, 16, 64, 256, 1024):
-            best = 0.0
-            for _ in range(5):
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                hb.hisparse_probe_host_read(stream, ptr, dev.data_ptr(), nbytes, wgs)
-                torch.cuda.synchronize()
-                best = max(best, nbytes / (time.perf_counter() - t0) / 1e9)
-            per_wg[wgs] = round(best, 2)
+            per_wg[wgs] = best_of(
+                lambda: hb.hisparse_probe_host_read(stream, ptr, dev.data_ptr(), nbytes, wgs))
         res["zero_copy_read_GBps"] = per_wg
+        del src, view
     finally:
         hb.hisparse_host_free(ptr)
+    pinned = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    pinned.fill_(1)
+    res["memcpy_h2d_torch_pinned_GBps"] = best_of(lambda: dev.copy_(pinned, non_blocking=True))
+    del pinned
     res["measured_peak_GBps"] = max(res["memcpy_h2d_GBps"], *res["zero_copy_read_GBps"].values())
     return res
 
@@ -411,7 +446,24 @@ def committed_traffic(kernels, label, mode):
             return None
         scale = (CALIBRATION_BYTES / 1024.0) / got["probe_host_read_kernel"]
         vals[counter] = sum(got[k] for k in kernels) * scale * 1024.0
+        # the profiled run: its step and warm-up counts (dispatch means are
+        # over its launches, so the algorithmic bytes must be of the same steps)
+        cmd = re.search(r"^Command: `(.*)`$", text, re.M)
+        cmd = cmd.group(1) if cmd else ""
+        st = re.search(r"--steps (\d+)", cmd)
+        wu = re.search(r"--warmup (\d+)", cmd)
+        vals.setdefault("profiled", []).append({
+            "counter": counter, "steps": int(st.group(1)) if st else None,
+            "warmup": int(wu.group(1)) if wu else None, "serial": "--serial" in cmd})
     return vals
+
+
+def traffic_matches(t, K, serial):
+    """True when every counter run of `t` profiled exactly K steps with no
+    warm-up on the same schedule, i.e. its per-dispatch means are over the
+    launches whose algorithmic bytes this run computes."""
+    return bool(t) and all(p["steps"] == K and p["warmup"] == 0 and p["serial"] == serial
+                           for p in t["profiled"])
 
 
 def traffic_fields(t):
@@ -517,6 +569,41 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
             "mode": "one HIP graph per schedule, best of 2 replays from a cold cache"}
 
 
+def _mla_cpu_baseline(setup, K, q_np, rows, Q, per, scale):
+    """The float64 oracle attention on the host over the host rows at the
+    last step's selections, for as many attention rows as fit ~10 s (at
+    least one): (seconds, rows timed)."""
+    from oracle.attention import bf16_to_f64, mla_decode_attention_lse
+    t_cpu, n_cpu = 0.0, 0
+    for r in range(rows):
+        b, j = divmod(r, Q)
+        sel = setup.trace[K - 1, 0, b].reshape(Q, per)[j]
+        host = setup.hosts[(b, 0)][1]
+        tok = host[sel[sel >= 0]].reshape(-1, 1152)
+        t0 = time.perf_counter()
+        mla_decode_attention_lse(bf16_to_f64(q_np[r]), bf16_to_f64(tok), scale)
+        t_cpu += time.perf_counter() - t0
+        n_cpu += 1
+        if t_cpu > 10.0:
+            break
+    return t_cpu, n_cpu
+
+
+def _topk_cpu_baseline(scores, N, k):
+    """The top-k oracle on the host, one row at a time, for as many rows as
+    fit ~10 s (at least one): (seconds, rows timed)."""
+    from oracle.topk import topk_rows
+    t_cpu, n_cpu = 0.0, 0
+    for b in range(scores.shape[0]):
+        t0 = time.perf_counter()
+        topk_rows(scores[b:b + 1], [N], k)
+        t_cpu += time.perf_counter() - t0
+        n_cpu += 1
+        if t_cpu > 10.0:
+            break
+    return t_cpu, n_cpu
+
+
 def mla_study(setup, K, H):
     """Sparse MLA decode attention over the slot map of layer 0, after each of
     K resolve steps; timed with torch events on the launching stream.  With
@@ -557,21 +644,7 @@ def mla_study(setup, K, H):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) * 1e3)
     us = float(np.median(times[1:] if len(times) > 1 else times))
-    # the float64 oracle attention on the host, over the host rows at the last
-    # step's selections, for as many requests as fit ~10 s (at least one)
-    from oracle.attention import bf16_to_f64, mla_decode_attention_lse
-    t_cpu, n_cpu = 0.0, 0
-    for r in range(rows):
-        b, j = divmod(r, Q)
-        sel = setup.trace[K - 1, 0, b].reshape(Q, per)[j]
-        host = setup.hosts[(b, 0)][1]
-        tok = host[sel[sel >= 0]].reshape(-1, 1152)
-        t0 = time.perf_counter()
-        mla_decode_attention_lse(bf16_to_f64(q_np[r]), bf16_to_f64(tok), scale)
-        t_cpu += time.perf_counter() - t0
-        n_cpu += 1
-        if t_cpu > 10.0:
-            break
+    t_cpu, n_cpu = _mla_cpu_baseline(setup, K, q_np, rows, Q, per, scale)
     cpu_us_per_call = t_cpu / n_cpu * rows * 1e6
     n_tok = per * T
     byts = rows * n_tok * 1152 + rows * H * (1152 + 512 * 4 + 4)
@@ -606,7 +679,6 @@ def topk_study(cfg, K, W):
     (histogram, filter), so at best half the HBM peak is reachable."""
     import torch
     from hierarchical_kv_cache_hisparse_amd import binding as hb
-    from oracle.topk import topk_rows
     from workload.scores import score_rows
     B, N, k = cfg.B, cfg.L0, cfg.k
     stride = ((N + 3) // 4) * 4
@@ -653,22 +725,7 @@ def topk_study(cfg, K, W):
         g.replay()
     torch.cuda.synchronize()
     graph_us = (time.perf_counter() - t0) / (5 * 16) * 1e6
-    # parity spot check of the last eager result
-    want = topk_rows(host_scores[(K - 1) % n_sets], [N] * B, k)
-    got = None
-    call(K - 1)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy()
-    assert np.array_equal(got, want), "top-k result differs from the oracle"
-    # the oracle on the host: as many rows as fit ~10 s (at least one)
-    t_cpu, n_cpu = 0.0, 0
-    for b in range(B):
-        t0 = time.perf_counter()
-        topk_rows(host_scores[0][b:b + 1], [N], k)
-        t_cpu += time.perf_counter() - t0
-        n_cpu += 1
-        if t_cpu > 10.0:
-            break
+    t_cpu, n_cpu = _topk_cpu_baseline(host_scores[0], N, k)
     byts = B * N * 4 + B * k * 4
     return {"metric": "top-k selection over indexer scores", "value": round(us, 3),
             "unit": "us per layer call", "higher_is_better": False, "workload": cfg.name,
@@ -883,7 +940,7 @@ def main():
     if Q > 1:   # Q query tokens, each with the workload's k selections
         cfg = cfg.scaled(k=Q * base.k)
     host_flags = hb.HISPARSE_HOST_NONCOHERENT if args.host_noncoherent else hb.HISPARSE_HOST_COHERENT
-    setup = Setup(cfg, host_flags, queries=Q)
+    setup = Setup(cfg, host_flags, queries=Q, numa_node=args.numa_node, prefetch=not args.serial)
     K, W = args.steps, args.warmup
     io = setup.noio if (args.no_io and args.only_timed) else setup.io
     if args.pipeline:
@@ -961,7 +1018,9 @@ def main():
             assert tuple(int(x) for x in setup.totals(io)) == (tot_miss, tot_evict, tot_hit), \
                 "graph replay and eager pass disagree"
             del graph
-            mode = "one HIP graph of all K steps, one timed replay from a cold cache"
+            mode = "one HIP graph of all K steps, one timed replay from a cold cache" + (
+                "; every layer l+1 prefetched on a second stream (forked after layer l) and "
+                "joined by its resolve" if setup.prefetch else "")
             log(f"timed: {K} steps in {elapsed * 1e3:.3f} ms (graph replay)")
         value = entries / elapsed
 
@@ -971,8 +1030,10 @@ def main():
         fused = timing["fetch_launches"] == 0
         resolve_avg_s = timing["resolve_ms"] / max(1, timing["resolve_launches"]) / 1e3
         # one launch per layer call (the resolve kernel, with the append fused
-        # in when the context grows): then the timed graph holds nothing else
-        one_launch = fused and (not cfg.growth or cfg.R > 0)
+        # in when the context grows): then the timed graph holds nothing else.
+        # The prefetch schedule adds a join launch per prefetched layer, so
+        # there the eager pass's per-launch events are used.
+        one_launch = fused and (not cfg.growth or cfg.R > 0) and not setup.prefetch
         launch_timing = "eager pass, library HIP events around each launch"
         if fused:   # the resolve workgroups copy their own misses
             fetch_avg_s = resolve_avg_s
@@ -995,6 +1056,13 @@ def main():
         dominant = "resolve_kernel" if fused else "fetch_kernel"
         alg_traffic = 2 * fetch_bytes_per_launch + (meta_bytes if fused else 0)
         traffic = committed_traffic(dominant, cfg.label, "fused" if fused else "split")
+        # counters are reported only when taken over the same K steps (from a
+        # cold cache, no warm-up) and schedule as this run
+        traffic_note = None
+        if traffic and not traffic_matches(traffic, K, not setup.prefetch):
+            traffic_note = (f"counter summaries were taken over another step count or schedule "
+                            f"({traffic['profiled']}); this run has {K} steps")
+            traffic = None
 
         result = {
             "metric": "resolved top-k entries/s; miss-fetch GB/s vs host-link peak; no-IO overhead",
@@ -1013,6 +1081,8 @@ def main():
                        "context_rows": cfg.L0, "row_bytes": cfg.row_bytes, "cache_slots": cfg.C,
                        "resident_window": cfg.R, "top_k": cfg.k, "steps": K,
                        "carry_over_pct": cfg.carry_pct, "replacement": cfg.replacement,
+                       "shared_selection": cfg.shared_selection,
+                       "schedule": "layer-wise prefetch" if setup.prefetch else "serial",
                        "timed_launch_mode": mode},
             "roofline": {"bound": "host_link", "kernel": dominant, "fused_fetch": fused,
                          "bound_note": "the miss fetch moves missed rows from pinned host memory "
@@ -1032,6 +1102,11 @@ def main():
                          "traffic_over_algorithmic": (
                              round((traffic["FETCH_SIZE"] + traffic["WRITE_SIZE"]) / alg_traffic, 3)
                              if traffic else None),
+                         "traffic_source": (
+                             f"rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE summaries "
+                             f"profiles/pmc_{{fetch,write}}_size_{cfg.label}_"
+                             f"{'fused' if fused else 'split'}.md, {K} steps from a cold cache, "
+                             f"scaled by the 256 MiB device copy" if traffic else traffic_note),
                          "avg_launch_us": round(fetch_avg_s * 1e6, 3),
                          "launch_timing": launch_timing,
                          "avg_launch_us_eager": round(
@@ -1104,7 +1179,7 @@ def main():
             # copies suppressed, every layer call is one launch (the append is
             # fused in when the context grows and a window exists): the graph's
             # nodes are the K x layers resolve launches
-            if not cfg.growth or cfg.R > 0:
+            if (not cfg.growth or cfg.R > 0) and not setup.prefetch:
                 rk_us = ev_noio_ms * 1e3 / (K * cfg.layers)
                 rk["launch_timing"] = ("HIP events around the copy-free graph replay (best of 3), "
                                        "whose K x layers nodes are the resolve launches")
@@ -1116,6 +1191,8 @@ def main():
             rk["achieved"] = round(meta_bytes / (rk_us * 1e-6) / 1e9, 3)
             rk["frac"] = round(rk["achieved"] / HBM_PEAK_GBPS, 6)
             t_meta = committed_traffic("resolve_kernel", cfg.label, "noio")
+            if t_meta and not traffic_matches(t_meta, K, not setup.prefetch):
+                t_meta = None
             rk["traffic"] = round(t_meta["FETCH_SIZE"] + t_meta["WRITE_SIZE"]) if t_meta else None
             rk["traffic_read_bytes"] = round(t_meta["FETCH_SIZE"]) if t_meta else None
             rk["traffic_write_bytes"] = round(t_meta["WRITE_SIZE"]) if t_meta else None
@@ -1164,12 +1241,22 @@ def main():
                                        if dt0_io > dt0_noio else None),
                 "mode": "step 0 alone from a cold cache, one HIP graph, best of 3"}
             if not args.no_probe:
-                lp = link_probe(torch, hb)
+                lp = link_probe(torch, hb, args.numa_node)
                 result["link_peak"] = lp
                 result["roofline"]["peak_measured"] = lp["measured_peak_GBps"]
                 result["roofline"]["frac_of_measured"] = round(fetch_gbps / lp["measured_peak_GBps"], 4)
                 cs = result["miss_fetch"]["cold_step"]
                 cs["frac_of_measured"] = round(cs["GBps"] / lp["measured_peak_GBps"], 4)
+            if setup.prefetch and not args.no_prefetch_study:
+                # the pages' claim for shared selections: prefetching the next
+                # layer during this layer's compute hides part of the misses
+                result["prefetch"] = {
+                    "stand_in_compute": prefetch_study(setup, K, args.layer_compute_us, "busy"),
+                    "attention_compute": prefetch_study(setup, K, 0.0, "attention",
+                                                        args.heads)}
+                log("prefetch study: hidden fraction {} (stand-in compute), {} (attention)".format(
+                    result["prefetch"]["stand_in_compute"]["value"],
+                    result["prefetch"]["attention_compute"]["value"]))
             if not args.no_cpu_baseline:
                 result["cpu_baseline"] = cpu_baseline(setup, K, no_io_seconds=3.0)
                 result["cpu_baseline_threads"] = cpu_baseline(

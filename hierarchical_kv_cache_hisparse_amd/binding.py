@@ -34,6 +34,9 @@ HISPARSE_STATUS_PREFETCH_MISMATCH = 0x8
 HISPARSE_HOST_COHERENT = 0x0
 HISPARSE_HOST_NONCOHERENT = 0x1
 
+HISPARSE_NUMA_DEVICE = -1      # the NUMA node closest to the current device
+HISPARSE_NUMA_DEFAULT = -2     # the process's own memory policy
+
 # Per-stream header words (int32) in the metadata buffer.
 HDR_T, HDR_STATUS, HDR_PAD, HDR_RES, HDR_HIT, HDR_MISS, HDR_EVICT, HDR_BYTES = range(8)
 HDR_TOTAL_MISS, HDR_TOTAL_EVICT, HDR_TOTAL_HIT = 8, 10, 12   # int64 word pairs
@@ -96,7 +99,9 @@ def library():
         sig = {
             "hisparse_workspace_bytes": [P, P, P],
             "hisparse_meta_layout_of": [P, P],
-            "hisparse_host_alloc": [SZ, U32, P],
+            "hisparse_host_alloc": [SZ, ctypes.c_int, U32, P],
+            "hisparse_host_numa_node": [P, P],
+            "hisparse_device_numa_node": [P],
             "hisparse_host_free": [P],
             "hisparse_create": [P, P, P, P, P],
             "hisparse_destroy": [P],
@@ -160,10 +165,25 @@ def hisparse_meta_layout_of(cfg: hisparse_config) -> hisparse_meta_layout:
     return out
 
 
-def hisparse_host_alloc(nbytes: int, flags: int = HISPARSE_HOST_COHERENT) -> int:
+def hisparse_host_alloc(nbytes: int, flags: int = HISPARSE_HOST_COHERENT,
+                        numa_node: int = HISPARSE_NUMA_DEVICE) -> int:
     ptr = ctypes.c_void_p()
-    _check(library().hisparse_host_alloc(nbytes, flags, ctypes.byref(ptr)), "hisparse_host_alloc")
+    _check(library().hisparse_host_alloc(nbytes, numa_node, flags, ctypes.byref(ptr)),
+           "hisparse_host_alloc")
     return ptr.value
+
+
+def hisparse_host_numa_node(host_ptr: int) -> int:
+    node = ctypes.c_int()
+    _check(library().hisparse_host_numa_node(host_ptr, ctypes.byref(node)),
+           "hisparse_host_numa_node")
+    return node.value
+
+
+def hisparse_device_numa_node() -> int:
+    node = ctypes.c_int()
+    _check(library().hisparse_device_numa_node(ctypes.byref(node)), "hisparse_device_numa_node")
+    return node.value
 
 
 def hisparse_host_free(ptr: int) -> None:

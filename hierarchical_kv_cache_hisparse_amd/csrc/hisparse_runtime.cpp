@@ -8,7 +8,11 @@
 // Hierarchical KV Cache Management", Abstract: resolution runs inside the
 // decode graph; "Hybrid HiSparse", Timeline: the kernel is graph-capturable).
 #include <hip/hip_runtime_api.h>
+#include <linux/mempolicy.h>
+#include <sys/syscall.h>
+#include <unistd.h>
 
+#include <cerrno>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -47,6 +51,8 @@ int hip_fail(hipError_t e, const char* what) {
     hipError_t e_ = (call);                     \
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
+
+constexpr int kMaxNumaNodes = 1024;  // node masks handed to the memory-policy calls
 
 constexpr uint32_t kKnownFlags =
     HISPARSE_NO_IO | HISPARSE_DEBUG_VALIDATE | HISPARSE_SERIALIZE_PREFETCH;
@@ -266,21 +272,84 @@ int hisparse_meta_layout_of(const hisparse_config* cfg, hisparse_meta_layout* ou
   return HISPARSE_OK;
 }
 
-int hisparse_host_alloc(size_t bytes, uint32_t flags, void** host_ptr) {
+int hisparse_device_numa_node(int* node) {
+  if (!node) return fail(HISPARSE_ERR_INVALID_ARG, "node is NULL");
+  *node = -1;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  int id = -1;
+  if (hipDeviceGetAttribute(&id, hipDeviceAttributeHostNumaId, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    id = -1;
+  }
+  *node = id >= 0 ? id : -1;
+  return HISPARSE_OK;
+}
+
+int hisparse_host_numa_node(const void* host_ptr, int* node) {
+  if (!host_ptr || !node) return fail(HISPARSE_ERR_INVALID_ARG, "NULL argument");
+  *node = -1;
+  int n = -1;
+  // the node of the page holding host_ptr (MPOL_F_NODE | MPOL_F_ADDR)
+  if (syscall(SYS_get_mempolicy, &n, nullptr, 0UL, const_cast<void*>(host_ptr),
+              (unsigned long)(MPOL_F_NODE | MPOL_F_ADDR)) != 0)
+    return fail(HISPARSE_ERR_INVALID_ARG, "get_mempolicy on %p failed: %s", host_ptr,
+                strerror(errno));
+  *node = n;
+  return HISPARSE_OK;
+}
+
+int hisparse_host_alloc(size_t bytes, int numa_node, uint32_t flags, void** host_ptr) {
   if (!host_ptr) return fail(HISPARSE_ERR_INVALID_ARG, "host_ptr is NULL");
   *host_ptr = nullptr;
   if (bytes == 0) return fail(HISPARSE_ERR_INVALID_ARG, "bytes is 0");
   if (flags & ~HISPARSE_HOST_NONCOHERENT)
     return fail(HISPARSE_ERR_INVALID_ARG, "unknown host flags 0x%x", flags);
+  if (numa_node < HISPARSE_NUMA_DEFAULT || numa_node >= kMaxNumaNodes)
+    return fail(HISPARSE_ERR_INVALID_ARG, "numa_node %d outside [%d, %d)", numa_node,
+                HISPARSE_NUMA_DEFAULT, kMaxNumaNodes);
+  int node = numa_node;
+  if (node == HISPARSE_NUMA_DEVICE) {
+    int rc = hisparse_device_numa_node(&node);
+    if (rc) return rc;  // node stays -1 when the device reports none
+  }
   unsigned hf = hipHostMallocMapped | hipHostMallocPortable |
                 ((flags & HISPARSE_HOST_NONCOHERENT) ? hipHostMallocNonCoherent
                                                      : hipHostMallocCoherent);
+  // Placement: bind this thread's memory policy to `node` around the
+  // allocation, and tell HIP to follow that policy (hipHostMallocNumaUser);
+  // the previous policy is restored afterwards.
+  // A node asked for explicitly must be available; the device's own node is
+  // taken when the process may allocate there, else the allocation falls back
+  // to the process's policy (hisparse_host_numa_node tells where it landed).
+  unsigned long old_mask[kMaxNumaNodes / 64] = {0};
+  int old_mode = MPOL_DEFAULT;
+  bool bind = node >= 0;
+  if (bind) {
+    if (syscall(SYS_get_mempolicy, &old_mode, old_mask, (unsigned long)kMaxNumaNodes, nullptr,
+                0UL) != 0)
+      return fail(HISPARSE_ERR_INVALID_ARG, "get_mempolicy failed: %s", strerror(errno));
+    unsigned long mask[kMaxNumaNodes / 64] = {0};
+    mask[node / 64] = 1UL << (node % 64);
+    if (syscall(SYS_set_mempolicy, MPOL_BIND, mask, (unsigned long)kMaxNumaNodes) != 0) {
+      if (numa_node != HISPARSE_NUMA_DEVICE)
+        return fail(HISPARSE_ERR_INVALID_ARG, "cannot bind host memory to NUMA node %d: %s",
+                    node, strerror(errno));
+      bind = false;
+    }
+  }
+  if (bind) hf |= hipHostMallocNumaUser;
   hipError_t e = hipHostMalloc(host_ptr, bytes, hf);
+  if (bind) {
+    const bool had_mask = old_mode != MPOL_DEFAULT && old_mode != MPOL_LOCAL;
+    (void)syscall(SYS_set_mempolicy, old_mode, had_mask ? old_mask : nullptr,
+                  had_mask ? (unsigned long)kMaxNumaNodes : 0UL);
+  }
   if (e != hipSuccess) {
     (void)hipGetLastError();
     *host_ptr = nullptr;
-    return fail(HISPARSE_ERR_OOM, "hipHostMalloc of %zu bytes failed: %s", bytes,
-                hipGetErrorString(e));
+    return fail(HISPARSE_ERR_OOM, "hipHostMalloc of %zu bytes (NUMA node %d) failed: %s", bytes,
+                node, hipGetErrorString(e));
   }
   return HISPARSE_OK;
 }
@@ -492,6 +561,11 @@ int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, con
   if (int rc = check_no_overlap(h, sel, (size_t)h->cfg.num_requests * h->cfg.top_k, ctx_len,
                                 out_slot))
     return rc;
+  if (h->cfg.resident_window == 0 && h->pending[layer])
+    return fail(HISPARSE_ERR_STATE,
+                "layer %d has a pending prefetch and no resident window: the prefetch may "
+                "have read the appended row before it was written (append before prefetching)",
+                layer);
   if (h->cfg.resident_window == 0 || h->pending[layer]) {
     // the appended position may be fetched by this resolve (no window), or the
     // layer was resolved early: the append goes first, in its own launch

@@ -150,11 +150,34 @@ int hisparse_workspace_bytes(const hisparse_config* cfg, size_t* cache_bytes,
 int hisparse_meta_layout_of(const hisparse_config* cfg, hisparse_meta_layout* out);
 
 /* Allocate `bytes` of pinned, device-mapped host memory for a host history
- * (hipHostMalloc; HISPARSE_HOST_* flags).  [P3 Abstract: the full history
- * lives in host memory.]  The caller frees it with hisparse_host_free.
- * Errors: INVALID_ARG (bytes == 0 or bad flags), OOM. */
-int hisparse_host_alloc(size_t bytes, uint32_t flags, void** host_ptr);
+ * (hipHostMalloc; HISPARSE_HOST_* flags) on a NUMA node.  [P3 Abstract: the
+ * full history lives in host memory; every miss is read from it over the
+ * host link, so it belongs on the node next to the GPU.]
+ *   numa_node >= 0:        that node (the calling thread's memory policy is
+ *                          bound to it for the allocation, then restored);
+ *                          INVALID_ARG when the process may not use it;
+ *   HISPARSE_NUMA_DEVICE:  the node closest to the current HIP device
+ *                          (hipDeviceAttributeHostNumaId); when the device
+ *                          reports none or the process may not use it, the
+ *                          process's own policy applies;
+ *   HISPARSE_NUMA_DEFAULT: the process's own policy.
+ * hisparse_host_numa_node tells where the pages landed.  The caller frees
+ * the memory with hisparse_host_free.  Errors: INVALID_ARG (bytes == 0, bad
+ * flags, numa_node < -2 or >= 1024, node not usable), OOM, HIP. */
+#define HISPARSE_NUMA_DEVICE (-1)
+#define HISPARSE_NUMA_DEFAULT (-2)
+int hisparse_host_alloc(size_t bytes, int numa_node, uint32_t flags, void** host_ptr);
 int hisparse_host_free(void* host_ptr);
+
+/* NUMA node of the host page holding `host_ptr` (get_mempolicy with
+ * MPOL_F_NODE | MPOL_F_ADDR), e.g. to check where hisparse_host_alloc put a
+ * history.  Host only; no GPU needed.  Errors: INVALID_ARG (NULL, or an
+ * address the kernel cannot place). */
+int hisparse_host_numa_node(const void* host_ptr, int* node);
+
+/* NUMA node closest to the current HIP device, or -1 when the device
+ * reports none.  Errors: INVALID_ARG (NULL), HIP. */
+int hisparse_device_numa_node(int* node);
 
 /* Create a cache instance on the current HIP device.
  *   host_rows:   host pointers [num_layers * num_requests], entry l*B + b is
@@ -259,10 +282,12 @@ int hisparse_append(hisparse_t h, hipStream_t stream, int32_t layer, const void*
  * neither looks it up nor fetches it and the row stores run inside the
  * resolve launch; without a window, or when `layer` has a pending prefetch,
  * the two calls are made as separate launches.  A pending prefetch has
- * resolved the layer already: without a window the append must come before
- * that prefetch (hisparse_append), since the prefetch may fetch the appended
- * position.  Graph-capturable like hisparse_resolve.  Errors: INVALID_ARG,
- * HIP. */
+ * resolved the layer already: with a window the append then runs before the
+ * join; without a window the call is rejected (STATE), because that prefetch
+ * may have fetched the appended position's host row before it was written --
+ * append with hisparse_append before hisparse_prefetch instead.
+ * Graph-capturable like hisparse_resolve.  Errors: INVALID_ARG, STATE (no
+ * window and a pending prefetch on `layer`; nothing is launched), HIP. */
 int hisparse_append_resolve(hisparse_t h, hipStream_t stream, int32_t layer, const void* rows,
                             const int32_t* pos, const int32_t* sel, const int32_t* ctx_len,
                             int32_t* out_slot);

@@ -89,7 +89,7 @@ int main(int argc, char** argv) {
   LIB(hisparse_meta_layout_of(&cfg, &lay));
 
   void* host = NULL;
-  LIB(hisparse_host_alloc((size_t)L * ROW, HISPARSE_HOST_COHERENT, &host));
+  LIB(hisparse_host_alloc((size_t)L * ROW, HISPARSE_NUMA_DEVICE, HISPARSE_HOST_COHERENT, &host));
   unsigned char* rows = (unsigned char*)host;
   for (int p = 0; p < L; ++p)
     for (int j = 0; j < ROW; ++j) rows[p * ROW + j] = (unsigned char)(7 * p + j + 1);

@@ -1,99 +1,17 @@
 """GPU-side test plumbing: one libhisparse instance driven through the C ABI
 next to the CPU oracle on the same host buffers, with state read-back and
-element-by-element comparison.  Imported only by GPU tests, the smoke check
-and the benchmark.
+element-by-element comparison.  Imported only by GPU tests and the smoke
+check.
 """
 from __future__ import annotations
-
-import ctypes
 
 import numpy as np
 
 from hierarchical_kv_cache_hisparse_amd import binding as hb
+from hierarchical_kv_cache_hisparse_amd.instance import GpuInstance, host_view  # noqa: F401
 from tests.harness import OracleRun, appended_row, fill_host, make_trace
 from workload import rows as wrows
 from workload.configs import Workload
-
-
-def host_view(ptr: int, nbytes: int) -> np.ndarray:
-    return np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(ptr))
-
-
-class GpuInstance:
-    """A libhisparse handle over pinned host histories and torch device memory."""
-
-    def __init__(self, cfg: Workload, flags: int = 0, host_flags: int = hb.HISPARSE_HOST_COHERENT,
-                 device: str = "cuda:0", hosts=None):
-        import torch
-        self.torch = torch
-        self.cfg = cfg
-        self.device = device
-        self.flags = flags
-        self.hcfg = hb.make_config(cfg.B, cfg.layers, cfg.l_cap, cfg.row_bytes, cfg.C, cfg.R,
-                                   cfg.k, flags)
-        cache_bytes, meta_bytes = hb.hisparse_workspace_bytes(self.hcfg)
-        self.lay = hb.hisparse_meta_layout_of(self.hcfg)
-        nbytes = cfg.l_cap * cfg.row_bytes
-        self.owns_hosts = hosts is None
-        if hosts is None:
-            hosts = {}
-            for l in range(cfg.layers):
-                for b in range(cfg.B):
-                    ptr = hb.hisparse_host_alloc(nbytes, host_flags)
-                    hosts[(b, l)] = (ptr, host_view(ptr, nbytes).reshape(cfg.l_cap, cfg.row_bytes))
-        self.hosts = hosts
-        self.cache = torch.empty(cache_bytes, dtype=torch.uint8, device=device)
-        self.meta = torch.empty(meta_bytes, dtype=torch.uint8, device=device)
-        ptrs = [hosts[(b, l)][0] for l in range(cfg.layers) for b in range(cfg.B)]
-        self.h = hb.hisparse_create(self.hcfg, ptrs, self.cache.data_ptr(), self.meta.data_ptr())
-
-    def host(self, b: int, l: int) -> np.ndarray:
-        return self.hosts[(b, l)][1]
-
-    @property
-    def stream(self) -> int:
-        return self.torch.cuda.current_stream().cuda_stream
-
-    def close(self):
-        if self.h is not None:
-            hb.hisparse_destroy(self.h)
-            self.h = None
-        if self.owns_hosts:
-            for ptr, _ in self.hosts.values():
-                hb.hisparse_host_free(ptr)
-            self.hosts = {}
-
-    # -- state read-back ------------------------------------------------------
-    def _block(self, b: int, l: int):
-        return self.lay.stream_base + (l * self.cfg.B + b) * self.lay.stream_stride
-
-    def _i32(self, b, l, off, n):
-        start = self._block(b, l) + off
-        return self.meta[start: start + 4 * n].view(self.torch.int32).cpu().numpy()
-
-    def hdr(self, b, l):
-        return self._i32(b, l, self.lay.hdr, 16)
-
-    def state(self, b, l, with_pos2slot=True):
-        c = self.cfg
-        st = {"hdr": self.hdr(b, l),
-              "slot2pos": self._i32(b, l, self.lay.slot2pos, c.C),
-              "last_use": self._i32(b, l, self.lay.last_use, c.C),
-              "order": self._i32(b, l, self.lay.lru_order, c.C),
-              "evict": self._i32(b, l, self.lay.evict_log, 2 * c.k).reshape(c.k, 2),
-              "miss": self._i32(b, l, self.lay.miss_list, 2 * c.k).reshape(c.k, 2)}
-        if with_pos2slot:
-            st["pos2slot"] = self._i32(b, l, self.lay.pos2slot, c.l_cap)
-        return st
-
-    def slots(self, b, l) -> np.ndarray:
-        c = self.cfg
-        per = (c.C + c.R) * c.row_bytes
-        start = (l * c.B + b) * per
-        return self.cache[start: start + per].cpu().numpy().reshape(c.C + c.R, c.row_bytes)
-
-    def status(self, clear=False) -> int:
-        return hb.hisparse_get_status(self.h, clear)
 
 
 class LockstepRun:
@@ -177,18 +95,41 @@ class LockstepRun:
                 hb.hisparse_resolve(self.gpu.h, self.gpu.stream, self.sel_dev[s, l].data_ptr(),
                                     self.ctx_dev[s].data_ptr(), l, self.out_dev[l].data_ptr())
 
+    def prefetch_step(self, s: int, main: int, side: int, sel=None, ctx=None, out=None):
+        """Step s with the layer-wise prefetch schedule of shared selections:
+        resolve layer 0 on `main`; then for every layer l, prefetch layer l+1
+        on `side` (forked from `main` after layer l's call) and resolve layer
+        l+1 on `main`, which joins the prefetch.  sel / ctx / out default to
+        this run's buffers for step s (a graph passes fixed buffers)."""
+        sel = self.sel_dev[s] if sel is None else sel
+        ctx = self.ctx_dev[s] if ctx is None else ctx
+        out = self.out_dev if out is None else out
+        h = self.gpu.h
+        hb.hisparse_resolve(h, main, sel[0].data_ptr(), ctx.data_ptr(), 0, out[0].data_ptr())
+        for l in range(self.cfg.layers - 1):
+            hb.hisparse_prefetch(h, main, side, sel[l + 1].data_ptr(), ctx.data_ptr(), l + 1)
+            hb.hisparse_resolve(h, main, sel[l + 1].data_ptr(), ctx.data_ptr(), l + 1,
+                                out[l + 1].data_ptr())
+
     def oracle_step(self, s: int):
         return self.oracle.step(s, self.trace, no_io=self.no_io, queries=self.queries)
 
-    def compare_step(self, s: int, res, full_state=True, contents=True, host_rows=True):
-        """Element-by-element comparison of one step on every oracle stream."""
+    def compare_step(self, s: int, res, full_state=True, contents=True, host_rows=True,
+                     full_streams=None):
+        """Element-by-element comparison of one step on every oracle stream:
+        slot map, clock, counters, eviction log, miss list, slot2pos, last_use
+        and LRU order always; with full_state the position->slot table and
+        with contents the slot bytes, on `full_streams` (default: all of
+        them).  The metadata buffer is read once."""
         cfg = self.cfg
         out = self.out_dev.cpu().numpy()
+        snap = self.gpu.meta_snapshot()
         for (b, l), r in res.items():
             where = f"step {s} stream (b={b}, l={l})"
             assert r.status == 0, where
+            deep = full_streams is None or (b, l) in full_streams
             np.testing.assert_array_equal(out[l, b], r.out, err_msg=f"out_slot {where}")
-            g = self.gpu.state(b, l, with_pos2slot=full_state)
+            g = self.gpu.state(b, l, with_pos2slot=full_state and deep, snap=snap)
             hdr = g["hdr"]
             c = r.counters
             assert hdr[hb.HDR_T] == self.oracle.st[(b, l)].t[0], f"clock {where}"
@@ -209,10 +150,10 @@ class LockstepRun:
             # the maintained LRU order is the (last_use, slot) sort of the slots
             want_order = np.lexsort((np.arange(cfg.C), ost.last_use))
             np.testing.assert_array_equal(g["order"], want_order, err_msg=f"lru order {where}")
-            if full_state:
+            if full_state and deep:
                 np.testing.assert_array_equal(g["pos2slot"], ost.pos2slot,
                                               err_msg=f"pos2slot {where}")
-            if contents and not self.no_io:
+            if contents and deep and not self.no_io:
                 self.compare_contents(b, l, s, host_rows=host_rows)
 
     def compare_contents(self, b, l, s, host_rows=True):

@@ -1,46 +1,19 @@
 """Shared test plumbing: seeded workloads -> host rows -> oracle streams.
 
-Host rows of a stream are filled only where the trace can read them (its
-selections and resident windows); row p's bytes are a pure function of
-(data seed, request, layer, p), so this equals a full fill on every row that
-matters.  The oracle and the GPU library read the very same host buffers.
+The oracle and the GPU library read the very same host buffers; the host
+rows, traces and appended rows come from workload.prepare.
 """
 from __future__ import annotations
 
-import numpy as np
-
 from oracle.oracle import OracleStream, resolve_multi
-from workload import rows as wrows
 from workload.configs import Workload
-from workload.traces import full_trace, multi_query_trace, touched_positions
+from workload.prepare import appended_row, fill_host, make_trace  # noqa: F401
 
 
 def small_variant(cfg: Workload, **kw) -> Workload:
     """A reduced copy of a workload that keeps its structure (shared or
     independent selections, growth, window, row size, carry-over)."""
     return cfg.scaled(**kw)
-
-
-def make_trace(cfg: Workload, streams=None, queries: int = 1) -> np.ndarray:
-    if queries > 1:
-        return multi_query_trace(cfg, queries, streams=streams)
-    return full_trace(cfg, streams=streams)
-
-
-def fill_host(cfg: Workload, host_of, trace: np.ndarray, streams):
-    """Fill each stream's host rows that the trace can touch.
-
-    host_of(b, l) -> uint8 [l_cap, row_bytes] array (numpy or pinned view).
-    Appended rows (growth) are written later, at append time.
-    """
-    for (b, l) in streams:
-        pos = touched_positions(trace[:, l, b, :], cfg)
-        pos = pos[pos < cfg.L0]
-        wrows.fill_rows(host_of(b, l), cfg.row_elems, pos, cfg.data_seed, b, l)
-
-
-def appended_row(cfg: Workload, b: int, l: int, p: int) -> np.ndarray:
-    return wrows.make_row(cfg.row_elems, p, cfg.data_seed, b, l)
 
 
 class OracleRun:

@@ -114,6 +114,24 @@ def test_host_alloc_rejects_bad_arguments():
         hb.hisparse_host_alloc(0)
     with pytest.raises(hb.HisparseError):
         hb.hisparse_host_alloc(4096, 0x80)
+    for node in (-3, 1024):
+        with pytest.raises(hb.HisparseError) as e:
+            hb.hisparse_host_alloc(4096, hb.HISPARSE_HOST_COHERENT, node)
+        assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
+
+
+def test_host_numa_node_of_ordinary_host_memory():
+    """The page-placement query is host only: on a touched buffer it names a
+    node that exists on this machine, and it rejects NULL."""
+    import glob
+    import numpy as np
+    buf = np.ones(1 << 16, np.uint8)
+    node = hb.hisparse_host_numa_node(buf.ctypes.data)
+    nodes = {int(p.rsplit("node", 1)[1]) for p in glob.glob("/sys/devices/system/node/node[0-9]*")}
+    assert node in (nodes or {0}), (node, nodes)
+    with pytest.raises(hb.HisparseError) as e:
+        hb.hisparse_host_numa_node(None)
+    assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
 
 
 def test_topk_workspace_sizes():

@@ -94,3 +94,32 @@ def test_cpu_baseline_runs_the_oracle():
     assert r["kind"] == "oracle" and r["cores"] == 2 and r["unit"] == "entries/s"
     assert r["value"] > 0 and r["no_io_value"] > 0
     assert "trace of all 2 streams" in r["sample"]
+
+
+def test_only_the_cpu_baseline_legs_reach_the_oracle():
+    """The benchmark's setup and timed code have no import edge into oracle/
+    or tests/: every such import sits inside a function whose name says it
+    is a CPU-baseline leg, and importing the benchmark (and the package, the
+    instance helper and the input preparation it uses) loads neither."""
+    import ast
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+
+    def walk(node, fn=None):
+        for child in ast.iter_child_nodes(node):
+            name = child.name if isinstance(child, (ast.FunctionDef, ast.AsyncFunctionDef)) else fn
+            if isinstance(child, (ast.Import, ast.ImportFrom)):
+                mods = ([a.name for a in child.names] if isinstance(child, ast.Import)
+                        else [child.module or ""])
+                for m in mods:
+                    if m.split(".")[0] in ("oracle", "tests"):
+                        assert name and "cpu_baseline" in name, (m, name, child.lineno)
+            walk(child, name)
+
+    walk(tree)
+    code = ("import sys; sys.path.insert(0, %r); import bench; "
+            "import hierarchical_kv_cache_hisparse_amd.instance, workload.prepare; "
+            "bad = [m for m in sys.modules if m.split('.')[0] in ('oracle', 'tests')]; "
+            "assert not bad, bad" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                       cwd="/")
+    assert r.returncode == 0, r.stderr

@@ -234,6 +234,125 @@ def test_prefetch_with_a_growing_context():
         a.close()
 
 
+@pytest.mark.parametrize("captured", [False, True])
+def test_prefetch_schedule_against_the_oracle(captured):
+    """Shared selections, layer-wise prefetch: layer 0 resolved on the main
+    stream, then every layer l+1 prefetched on a second stream and joined by
+    its resolve.  Every step (eager, or one captured step replayed with
+    eager copies in between) is compared with the oracle resolving every
+    layer in order: slot maps, clocks, counters, eviction logs, LRU state,
+    position->slot tables and slot bytes of every stream."""
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import LockstepRun
+    cfg = WORKLOADS[4].scaled(B=3, layers=4, L0=30000, C=3000, k=1500, steps=10)
+    run = LockstepRun(cfg)
+    try:
+        main, side = torch.cuda.Stream(), torch.cuda.Stream()
+        sel_buf = torch.empty_like(run.sel_dev[0])
+        ctx_buf = torch.empty_like(run.ctx_dev[0])
+        graph = None
+        if captured:
+            graph = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(main):
+                with torch.cuda.graph(graph, stream=main):
+                    run.prefetch_step(0, main.cuda_stream, side.cuda_stream, sel=sel_buf,
+                                      ctx=ctx_buf)
+            torch.cuda.synchronize()
+        for s in range(cfg.steps):
+            if captured:
+                sel_buf.copy_(run.sel_dev[s])
+                ctx_buf.copy_(run.ctx_dev[s])
+                torch.cuda.synchronize()
+                graph.replay()
+            else:
+                torch.cuda.synchronize()
+                run.prefetch_step(s, main.cuda_stream, side.cuda_stream)
+            torch.cuda.synchronize()
+            run.compare_step(s, run.oracle_step(s))
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+
+
+def test_prefetch_over_a_growing_context_against_the_oracle():
+    """Shared selections over a context that grows by one row per step: each
+    layer's new row goes in through hisparse_append_resolve while the layer
+    after it is prefetched on a second stream (the pending layers append in
+    a launch of their own before the join).  Compared every step with the
+    oracle appending and resolving every layer in order, resident ring and
+    slot bytes included."""
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import LockstepRun
+    from tests.harness import appended_row
+    cfg = WORKLOADS[4].scaled(B=2, layers=3, L0=20000, growth=1, C=2500, k=1200, steps=7)
+    run = LockstepRun(cfg)
+    try:
+        main, side = torch.cuda.Stream(), torch.cuda.Stream()
+        h = run.gpu.h
+        for s in range(cfg.steps):
+            p = cfg.ctx_at(s) - 1
+            rows = torch.from_numpy(np.stack([
+                np.stack([appended_row(cfg, bb, l, p) for bb in range(cfg.B)])
+                for l in range(cfg.layers)])).to("cuda")
+            sel, ctx, pos, out = run.sel_dev[s], run.ctx_dev[s], run.pos_dev[s], run.out_dev
+            torch.cuda.synchronize()
+            ms, ss = main.cuda_stream, side.cuda_stream
+
+            def call(l):
+                if s > 0:
+                    hb.hisparse_append_resolve(h, ms, l, rows[l].data_ptr(), pos.data_ptr(),
+                                               sel[l].data_ptr(), ctx.data_ptr(),
+                                               out[l].data_ptr())
+                else:
+                    hb.hisparse_resolve(h, ms, sel[l].data_ptr(), ctx.data_ptr(), l,
+                                        out[l].data_ptr())
+
+            call(0)
+            for l in range(cfg.layers - 1):
+                hb.hisparse_prefetch(h, ms, ss, sel[l + 1].data_ptr(), ctx.data_ptr(), l + 1)
+                call(l + 1)
+            torch.cuda.synchronize()
+            if s > 0:
+                run.oracle.append(s)
+            run.compare_step(s, run.oracle_step(s))
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+
+
+def test_append_resolve_after_a_prefetch_without_a_window_is_rejected():
+    """Without a resident window the appended position may be selected, and
+    a pending prefetch may already have read its host row: the call is
+    rejected before anything is launched, and the prefetch can still be
+    joined."""
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import GpuInstance
+    cfg = WORKLOADS[1].scaled(layers=2, L0=5000, growth=1, C=512, k=256, steps=2)
+    g = GpuInstance(cfg)
+    try:
+        dev = "cuda:0"
+        ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device=dev)
+        pos = torch.full((cfg.B,), cfg.L0 - 1, dtype=torch.int32, device=dev)
+        sel = torch.from_numpy(np.random.default_rng(5).choice(cfg.L0, (cfg.B, cfg.k),
+                                                                replace=False).astype(np.int32)).to(dev)
+        rows = torch.zeros((cfg.B, cfg.row_bytes), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(sel)
+        side = torch.cuda.Stream()
+        s = g.stream
+        hb.hisparse_prefetch(g.h, s, side.cuda_stream, sel.data_ptr(), ctx.data_ptr(), 1)
+        with pytest.raises(hb.HisparseError) as e:
+            hb.hisparse_append_resolve(g.h, s, 1, rows.data_ptr(), pos.data_ptr(),
+                                       sel.data_ptr(), ctx.data_ptr(), out.data_ptr())
+        assert e.value.code == hb.HISPARSE_ERR_STATE
+        hb.hisparse_resolve(g.h, s, sel.data_ptr(), ctx.data_ptr(), 1, out.data_ptr())
+        torch.cuda.synchronize()
+        assert g.status() == 0
+        assert bool((out >= 0).all())
+    finally:
+        g.close()
+
+
 def test_prefetch_misuse_is_reported():
     torch, hb = _torch(), _hb()
     cfg = WORKLOADS[4].scaled(B=2, layers=2, L0=5000, steps=2)

@@ -137,4 +137,4 @@ WORKLOADS = {
 }
 
 # The workload the headline throughput is quoted on (fits one GPU).
-BENCH_WORKLOAD = 2
+BENCH_WORKLOAD = 4
