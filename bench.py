@@ -148,7 +148,9 @@ class Setup:
         fill_host(cfg, lambda b, l: self.hosts[(b, l)][1], self.trace, streams)
         # where the histories landed: the node of a few touched pages of the
         # first and last history, next to the GPU's own node
+        import glob
         self.host_memory["numa_node_requested"] = numa_node
+        self.host_memory["host_numa_nodes"] = len(glob.glob("/sys/devices/system/node/node[0-9]*"))
         self.host_memory["gpu_numa_node"] = hb.hisparse_device_numa_node()
         nodes = set()
         for key in (streams[0], streams[-1]):

@@ -292,10 +292,23 @@ int hisparse_host_numa_node(const void* host_ptr, int* node) {
   int n = -1;
   // the node of the page holding host_ptr (MPOL_F_NODE | MPOL_F_ADDR)
   if (syscall(SYS_get_mempolicy, &n, nullptr, 0UL, const_cast<void*>(host_ptr),
-              (unsigned long)(MPOL_F_NODE | MPOL_F_ADDR)) != 0)
-    return fail(HISPARSE_ERR_INVALID_ARG, "get_mempolicy on %p failed: %s", host_ptr,
-                strerror(errno));
-  *node = n;
+              (unsigned long)(MPOL_F_NODE | MPOL_F_ADDR)) == 0) {
+    *node = n;
+    return HISPARSE_OK;
+  }
+  // Pinned memory from the GPU driver is a device-file mapping whose pages
+  // the kernel does not place-query (EFAULT).  On a host with one NUMA node
+  // every page is on that node; otherwise the placement is unknown (-1).
+  int count = 0, only = -1;
+  for (int i = 0; i < kMaxNumaNodes; ++i) {
+    char path[64];
+    snprintf(path, sizeof(path), "/sys/devices/system/node/node%d", i);
+    if (access(path, F_OK) == 0) {
+      ++count;
+      only = i;
+    }
+  }
+  if (count == 1) *node = only;
   return HISPARSE_OK;
 }
 

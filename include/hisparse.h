@@ -171,8 +171,10 @@ int hisparse_host_free(void* host_ptr);
 
 /* NUMA node of the host page holding `host_ptr` (get_mempolicy with
  * MPOL_F_NODE | MPOL_F_ADDR), e.g. to check where hisparse_host_alloc put a
- * history.  Host only; no GPU needed.  Errors: INVALID_ARG (NULL, or an
- * address the kernel cannot place). */
+ * history.  Pinned memory from the GPU driver is a device-file mapping the
+ * kernel does not place-query: then *node is the host's only node when it
+ * has one, else -1 (unknown).  Host only; no GPU needed.  Errors:
+ * INVALID_ARG (NULL). */
 int hisparse_host_numa_node(const void* host_ptr, int* node);
 
 /* NUMA node closest to the current HIP device, or -1 when the device

@@ -129,6 +129,10 @@ def test_host_numa_node_of_ordinary_host_memory():
     node = hb.hisparse_host_numa_node(buf.ctypes.data)
     nodes = {int(p.rsplit("node", 1)[1]) for p in glob.glob("/sys/devices/system/node/node[0-9]*")}
     assert node in (nodes or {0}), (node, nodes)
+    # a page the kernel cannot place-query (nothing mapped there): the only
+    # node of a one-node host, else unknown
+    fallback = hb.hisparse_host_numa_node(16)
+    assert fallback == (next(iter(nodes)) if len(nodes) == 1 else -1), (fallback, nodes)
     with pytest.raises(hb.HisparseError) as e:
         hb.hisparse_host_numa_node(None)
     assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
