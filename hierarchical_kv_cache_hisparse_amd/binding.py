@@ -122,6 +122,7 @@ def library():
             "hisparse_mla_workspace_bytes_multi": [P, I32, I32, I32, P],
             "hisparse_sparse_mla_decode_multi": [P, P, I32, I32, I32, P, P, I32, ctypes.c_float, P,
                                                  P, P],
+            "hisparse_sparse_mla_decode_noalloc": [P, P, I32, P, P, I32, ctypes.c_float, P, P],
             "hisparse_topk_workspace_bytes": [I32, ctypes.c_int64, P],
             "hisparse_topk": [P, P, ctypes.c_int64, I32, ctypes.c_int64, P, I32, P, P],
         }
@@ -290,6 +291,16 @@ def hisparse_sparse_mla_decode(h, stream: int, layer: int, q: int, out_slot: int
     _check(library().hisparse_sparse_mla_decode(h, stream, layer, q, out_slot, num_heads,
                                                 scale, workspace, out, lse),
            "hisparse_sparse_mla_decode")
+
+
+HISPARSE_NOALLOC_SCRATCH_BYTES = 40 << 20
+
+
+def hisparse_sparse_mla_decode_noalloc(h, stream: int, layer: int, q: int, out_slot: int,
+                                       num_heads: int, scale: float, out: int, lse: int) -> None:
+    _check(library().hisparse_sparse_mla_decode_noalloc(h, stream, layer, q, out_slot, num_heads,
+                                                        scale, out, lse),
+           "hisparse_sparse_mla_decode_noalloc")
 
 
 def hisparse_mla_workspace_bytes_multi(h, queries: int, per_query: int, num_heads: int) -> int:

@@ -17,7 +17,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-paramet
 # Device code: gfx950 only; packed FP32 instructions are switched off.
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = [("hisparse_kernels.hip", True), ("hisparse_mla.hip", True), ("hisparse_topk.hip", True),
-           ("hisparse_runtime.cpp", False)]
+           ("hisparse_noalloc.hip", True), ("hisparse_runtime.cpp", False)]
 
 
 def build(verbose: bool = False) -> str:

@@ -22,6 +22,7 @@
 #include <vector>
 
 #include "hisparse.h"
+#include "hisparse_entry.h"
 #include "hisparse_internal.h"
 #include "hisparse_mla_internal.h"
 #include "hisparse_topk_internal.h"
@@ -109,6 +110,18 @@ struct TimedCall {
 
 }  // namespace
 
+namespace hsp {
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+}  // namespace hsp
+
 struct hisparse {
   hisparse_config cfg;
   hisparse_meta_layout lay;
@@ -127,6 +140,10 @@ struct hisparse {
   size_t pool_used = 0;
   hisparse_timing totals{};
 };
+
+namespace hsp {
+int handle_device(const hisparse* h) { return h ? h->device : -1; }
+}  // namespace hsp
 
 namespace {
 
@@ -413,6 +430,10 @@ int hisparse_create(const hisparse_config* cfg, void* const* host_rows, void* de
       return fail(HISPARSE_ERR_UNSUPPORTED, "C=%d, k=%d need %zu bytes of LDS; the device has %d",
                   cfg->cache_slots, cfg->top_k, sh.lds_bytes, lds_max);
     }
+  }
+  if (int rc2 = noalloc_setup(h->device)) {
+    release(h);
+    return rc2;
   }
   h->pending.assign(L, 0);
   h->ev_fork.assign(L, nullptr);

@@ -383,6 +383,26 @@ int hisparse_sparse_mla_decode_multi(hisparse_t h, hipStream_t stream, int32_t l
                                      const int32_t* out_slot, int32_t num_heads, float scale,
                                      void* workspace, float* out, float* lse);
 
+/* ---- the attention for callers that cannot allocate ------------------------
+ * For code that may not call hipMalloc or any allocating routine: work under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * hisparse_sparse_mla_decode_noalloc is hisparse_sparse_mla_decode without
+ * the workspace argument: the per-split partials live in a fixed device array
+ * of HISPARSE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends (its address is looked up when a handle is created
+ * on that GPU).  The caller still passes q, out_slot, out and lse.  A call
+ * whose workspace (hisparse_mla_workspace_bytes) exceeds the array is
+ * rejected with UNSUPPORTED before anything is launched; the array needs no
+ * initialisation.  All calls on one GPU share its array: calls that overlap
+ * in time on one GPU (streams not ordered with each other, several handles
+ * included) race on it and must be ordered by the caller.  Errors: as
+ * hisparse_sparse_mla_decode, and UNSUPPORTED for a workspace beyond the
+ * array. */
+#define HISPARSE_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+int hisparse_sparse_mla_decode_noalloc(hisparse_t h, hipStream_t stream, int32_t layer,
+                                       const void* q, const int32_t* out_slot, int32_t num_heads,
+                                       float scale, float* out, float* lse);
+
 /* ---- top-k selection over indexer scores ----------------------------------
  * The step before resolution: from one score per position (a token for
  * DSA-style per-layer selection, a 16-token page for Quest-style selection),
