@@ -34,6 +34,7 @@ constexpr int kMaxSlots = 16384;
 constexpr int kMaxRequests = 32768;   // the fetch kernel keeps B+1 prefixes in LDS
 constexpr size_t kMaxLdsBytes = 163840;   // gfx950: 160 KiB of LDS per workgroup
 constexpr int kFetchThreads = 256;
+constexpr int kFetchStreamSlices = 8;  // below this many streams the fetch grid is sliced per stream
 
 
 // Byte layout of the metadata buffer (mirrors hisparse_meta_layout).
@@ -91,11 +92,15 @@ ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries 
 // Kernel launchers (hisparse_kernels.hip).  All are asynchronous on `s`.
 hipError_t launch_init(const StreamView& v, hipStream_t s, int layer, int request,
                        bool clear_status);
+// ev0 / ev1 (optional): events taking the start and end time of the kernel
+// itself (eager calls only, not under capture).
 hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const int32_t* sel,
                           const int32_t* ctx_len, int32_t* out, int32_t* sel_copy,
                           int multi_entries = 0, const uint8_t* app_rows = nullptr,
-                          const int32_t* app_pos = nullptr);
-hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid_x);
+                          const int32_t* app_pos = nullptr, hipEvent_t ev0 = nullptr,
+                          hipEvent_t ev1 = nullptr);
+hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid_x,
+                        hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_prefetch_join(const StreamView& v, hipStream_t s, const int32_t* sel,
                                 const int32_t* sel_copy, const int32_t* pf_out, int32_t* out);
 hipError_t launch_load_window(const StreamView& v, hipStream_t s, int layer,

@@ -36,6 +36,7 @@
 //     (a separate instantiation), since with a resident window it is never
 //     looked up or fetched by the resolution.
 //   No MFMA anywhere: nothing here is a contraction.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "hisparse_device.h"
@@ -592,6 +593,97 @@ __global__ void __launch_bounds__(kFetchThreads) fetch_kernel(StreamView v, int 
 }
 
 // ---------------------------------------------------------------------------
+// Miss fetch for calls of few streams: a slice of the grid per stream
+// (blockIdx.y).  A thread's chunks, and so the miss-list entries it copies,
+// follow from its index alone, so the first list entries are requested
+// together with the stream's miss count rather than after it (entries past
+// the count are stale but in bounds: the list holds k); then the host reads,
+// then the stores -- one dependent round trip fewer than the flat kernel
+// above, which needs every stream's count before it can place a chunk.
+//
+// The host reads and the slot stores are buffer instructions over the
+// stream's host history and slot rows: a chunk past the count gets an offset
+// beyond the buffer's range, which the hardware drops without a memory
+// request (a load returns zeros).  The code has no branch around any memory
+// instruction; branches around each load made the compiler wait for every
+// earlier memory operation, stores included, before the next load, and
+// plain loads at a dummy address would cost link traffic.  The host calls it
+// only when the history and the slot rows of a stream span < 4 GiB (32-bit
+// buffer offsets).
+// grid = (G, B)
+// ---------------------------------------------------------------------------
+constexpr uint32_t kBufferFormat = 0x00020000u;  // resource word 3 of a raw gfx9 buffer
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;    // past every resource's range (the host
+                                                 // checks each spans at most this), and
+                                                 // its four dwords do not wrap
+constexpr int kBufferNT = 2;                     // cache policy: non-temporal
+
+// `off` when `ok`, else kOutOfRange, by masks (no branch, no select chain)
+__device__ __forceinline__ uint32_t in_range(uint32_t off, bool ok) {
+  const uint32_t m = 0u - (uint32_t)ok;   // all ones when ok
+  return (off & m) | (kOutOfRange & ~m);
+}
+
+template <int U>
+__global__ void __launch_bounds__(kFetchThreads) fetch_stream_kernel(StreamView v, int layer) {
+  const int b = blockIdx.y;
+  const StreamPtrs st = stream_ptrs(v, layer, b);
+  const uint32_t rb = (uint32_t)v.row_bytes;
+  const uint32_t cpr = rb >> 4;
+  const uint32_t last = (uint32_t)v.k * cpr - 1;   // last chunk the miss list can name
+  const uint32_t stride = gridDim.x * kFetchThreads;
+  const int2* list = reinterpret_cast<const int2*>(st.miss);
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(v.host[layer * v.B + b]), 0, (int)((uint32_t)v.l_cap * rb),
+      (int)kBufferFormat);
+  const __amdgpu_buffer_rsrc_t dst = __builtin_amdgcn_make_buffer_rsrc(
+      v.cache + (int64_t)(layer * v.B + b) * (v.C + v.R) * v.row_bytes, 0,
+      (int)((uint32_t)(v.C + v.R) * rb), (int)kBufferFormat);
+  // The first batch is straight-line code, so the count is waited for only
+  // after its list reads are issued (in a loop the wait was hoisted above
+  // them); the rest (a cold step's misses) follows batch by batch.  A chunk
+  // past the count gets offset kOutOfRange by arithmetic, not by a branch.
+  const uint32_t g0 = blockIdx.x * kFetchThreads + threadIdx.x;
+  int2 e[U];
+  uint32_t c[U];
+  u32x4 val[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t g = min(g0 + u * stride, last);
+    e[u] = list[fast_div(g, cpr, v.cpr_magic, &c[u])];
+  }
+  const uint32_t total = (uint32_t)st.hdr[kHdrMiss] * cpr;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    val[u] = __builtin_amdgcn_raw_buffer_load_b128(
+        src, in_range((uint32_t)e[u].y * rb + 16 * c[u], g0 + u * stride < total), 0, kBufferNT);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        val[u], dst, in_range((uint32_t)e[u].x * rb + 16 * c[u], g0 + u * stride < total), 0, 0);
+  }
+  for (uint32_t gb = g0 + stride * U; gb < total; gb += stride * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t g = min(gb + u * stride, last);
+      e[u] = list[fast_div(g, cpr, v.cpr_magic, &c[u])];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      val[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          src, in_range((uint32_t)e[u].y * rb + 16 * c[u], gb + u * stride < total), 0,
+          kBufferNT);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      __builtin_amdgcn_raw_buffer_store_b128(
+          val[u], dst, in_range((uint32_t)e[u].x * rb + 16 * c[u], gb + u * stride < total), 0, 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // State reset: every slot empty, clock 0, LRU order 0..C-1.
 // grid = (chunks, requests, layers)
 // ---------------------------------------------------------------------------
@@ -665,16 +757,35 @@ __global__ void append_kernel(StreamView v, int layer, const uint8_t* __restrict
 
 // ---------------------------------------------------------------------------
 // Prefetch join: copy the prefetched slot map, check the selections match.
-// grid = B
+// One load round trip: every thread handles kJoinItems consecutive entries of
+// one request row (4 consecutive int32 per load when the row allows it).
+// grid = (ceil(k / (256 * kJoinItems)), B)
 // ---------------------------------------------------------------------------
-__global__ void prefetch_join_kernel(StreamView v, const int32_t* __restrict__ sel,
-                                     const int32_t* __restrict__ sel_copy,
-                                     const int32_t* __restrict__ pf_out, int32_t* __restrict__ out) {
-  const int64_t base = (int64_t)blockIdx.x * v.k;
+constexpr int kJoinItems = 4;
+
+__global__ void __launch_bounds__(256)
+    prefetch_join_kernel(StreamView v, const int32_t* __restrict__ sel,
+                         const int32_t* __restrict__ sel_copy,
+                         const int32_t* __restrict__ pf_out, int32_t* __restrict__ out,
+                         int vec) {
+  const int64_t base = (int64_t)blockIdx.y * v.k;
+  const int i0 = (blockIdx.x * 256 + threadIdx.x) * kJoinItems;
   int mismatch = 0;
-  for (int i = threadIdx.x; i < v.k; i += blockDim.x) {
-    mismatch |= sel[base + i] != sel_copy[base + i];
-    out[base + i] = pf_out[base + i];
+  if (vec && i0 < v.k) {   // k % 4 == 0, so i0 + 3 < k; every row start 16-byte aligned
+    const int4 a = *reinterpret_cast<const int4*>(sel + base + i0);
+    const int4 c = *reinterpret_cast<const int4*>(sel_copy + base + i0);
+    const int4 o = *reinterpret_cast<const int4*>(pf_out + base + i0);
+    mismatch = (a.x != c.x) | (a.y != c.y) | (a.z != c.z) | (a.w != c.w);
+    *reinterpret_cast<int4*>(out + base + i0) = o;
+  } else {
+#pragma unroll
+    for (int u = 0; u < kJoinItems; ++u) {
+      const int i = i0 + u;
+      if (i < v.k) {
+        mismatch |= sel[base + i] != sel_copy[base + i];
+        out[base + i] = pf_out[base + i];
+      }
+    }
   }
   if (__syncthreads_or(mismatch) && threadIdx.x == 0)
     atomicOr(status_word(v), HISPARSE_STATUS_PREFETCH_MISMATCH);
@@ -707,6 +818,21 @@ __global__ void __launch_bounds__(256) probe_host_read_kernel(const u32x4* __res
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+namespace {
+// A launch whose duration is timed by events attached to the kernel's own
+// dispatch (start and end of the kernel, as a profiler sees it) when ev0 or
+// ev1 is given; a plain launch otherwise (e.g. under graph capture).
+template <typename K, typename... Args>
+hipError_t launch_timed(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, hipEvent_t ev0,
+                        hipEvent_t ev1, Args... args) {
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev0, ev1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
+}  // namespace
+
 ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries) {
   // Fewest items per thread that fit 1024 threads; then the fewest 64-lane
   // waves that cover max(k, C) with that many items each.
@@ -735,20 +861,20 @@ ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries)
 
 hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const int32_t* sel,
                           const int32_t* ctx_len, int32_t* out, int32_t* sel_copy,
-                          int multi_entries, const uint8_t* app_rows, const int32_t* app_pos) {
+                          int multi_entries, const uint8_t* app_rows, const int32_t* app_pos,
+                          hipEvent_t ev0, hipEvent_t ev1) {
   const ResolveShape sh =
       resolve_shape(v.k, v.C, (v.flags & HISPARSE_DEBUG_VALIDATE) != 0, multi_entries);
   const dim3 grid(v.B), block(sh.threads);
   switch (sh.items) {
-#define HSP_RESOLVE_CASE(N)                                                                     \
-  case N:                                                                                       \
-    if (app_rows)                                                                               \
-      hipLaunchKernelGGL((resolve_kernel<N, true>), grid, block, sh.lds_bytes, s, v, layer, sel,  \
-                         ctx_len, out, sel_copy, multi_entries, app_rows, app_pos);             \
-    else                                                                                        \
-      hipLaunchKernelGGL((resolve_kernel<N, false>), grid, block, sh.lds_bytes, s, v, layer, sel, \
-                         ctx_len, out, sel_copy, multi_entries, app_rows, app_pos);             \
-    break;
+#define HSP_RESOLVE_CASE(N)                                                                    \
+  case N:                                                                                      \
+    return app_rows ? launch_timed(resolve_kernel<N, true>, grid, block, sh.lds_bytes, s, ev0,  \
+                                   ev1, v, layer, sel, ctx_len, out, sel_copy, multi_entries,   \
+                                   app_rows, app_pos)                                           \
+                    : launch_timed(resolve_kernel<N, false>, grid, block, sh.lds_bytes, s, ev0, \
+                                   ev1, v, layer, sel, ctx_len, out, sel_copy, multi_entries,   \
+                                   app_rows, app_pos);
     HSP_RESOLVE_CASE(1)
     HSP_RESOLVE_CASE(2)
     HSP_RESOLVE_CASE(3)
@@ -761,13 +887,20 @@ hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const i
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid) {
-  hipLaunchKernelGGL(fetch_kernel<4>, dim3(grid), dim3(kFetchThreads), sizeof(int) * (v.B + 1), s,
-                     v, layer);
-  return hipGetLastError();
+hipError_t launch_fetch(const StreamView& v, hipStream_t s, int layer, int grid, hipEvent_t ev0,
+                        hipEvent_t ev1) {
+  const uint64_t host_span = (uint64_t)v.l_cap * (uint64_t)v.row_bytes;
+  const uint64_t slot_span = (uint64_t)(v.C + v.R) * (uint64_t)v.row_bytes;
+  if (v.B < kFetchStreamSlices && host_span <= kOutOfRange && slot_span <= kOutOfRange) {
+    // few streams: a grid slice per stream (32-bit buffer offsets)
+    const int gx = grid / v.B > 1 ? grid / v.B : 1;
+    return launch_timed(fetch_stream_kernel<4>, dim3(gx, v.B), dim3(kFetchThreads), 0, s, ev0, ev1,
+                        v, layer);
+  }
+  return launch_timed(fetch_kernel<4>, dim3(grid), dim3(kFetchThreads), sizeof(int) * (v.B + 1), s,
+                      ev0, ev1, v, layer);
 }
 
 hipError_t launch_init(const StreamView& v, hipStream_t s, int layer, int request,
@@ -803,8 +936,16 @@ hipError_t launch_append(const StreamView& v, hipStream_t s, int layer, const ui
 
 hipError_t launch_prefetch_join(const StreamView& v, hipStream_t s, const int32_t* sel,
                                 const int32_t* sel_copy, const int32_t* pf_out, int32_t* out) {
-  hipLaunchKernelGGL(prefetch_join_kernel, dim3(v.B), dim3(256), 0, s, v, sel, sel_copy, pf_out,
-                     out);
+  // 16-byte vector accesses need every row start 16-byte aligned: k % 4 == 0
+  // and 16-byte aligned base pointers (the library's own buffers are)
+  const bool vec = (v.k & 3) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(sel) | reinterpret_cast<uintptr_t>(sel_copy) |
+                     reinterpret_cast<uintptr_t>(pf_out) | reinterpret_cast<uintptr_t>(out)) &
+                    15) == 0;
+  const int per = 256 * kJoinItems;
+  const dim3 grid((v.k + per - 1) / per, v.B);
+  hipLaunchKernelGGL(prefetch_join_kernel, grid, dim3(256), 0, s, v, sel, sel_copy, pf_out, out,
+                     vec ? 1 : 0);
   return hipGetLastError();
 }
 

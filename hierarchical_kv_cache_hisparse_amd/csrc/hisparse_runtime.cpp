@@ -104,7 +104,7 @@ int env_int(const char* name, int dflt) {
 }
 
 struct TimedCall {
-  hipEvent_t e0, e1, e2;  // before resolve, after resolve, after fetch
+  hipEvent_t e0, e1, e2, e3;  // resolve kernel start / end, fetch kernel start / end
   bool fetched;
 };
 
@@ -150,13 +150,13 @@ namespace {
 int fold_timing(hisparse* h) {
   for (size_t i = 0; i < h->pool_used; ++i) {
     TimedCall& c = h->pool[i];
-    HIP_TRY(hipEventSynchronize(c.fetched ? c.e2 : c.e1));
+    HIP_TRY(hipEventSynchronize(c.fetched ? c.e3 : c.e1));
     float ms = 0.f;
     HIP_TRY(hipEventElapsedTime(&ms, c.e0, c.e1));
     h->totals.resolve_ms += ms;
     h->totals.resolve_launches += 1;
     if (c.fetched) {
-      HIP_TRY(hipEventElapsedTime(&ms, c.e1, c.e2));
+      HIP_TRY(hipEventElapsedTime(&ms, c.e2, c.e3));
       h->totals.fetch_ms += ms;
       h->totals.fetch_launches += 1;
     }
@@ -184,15 +184,13 @@ int enqueue_resolve(hisparse* h, hipStream_t s, const int32_t* sel, const int32_
     }
     tc = &h->pool[h->pool_used++];
     tc->fetched = io && !h->view.fuse_fetch;
-    HIP_TRY(hipEventRecord(tc->e0, s));
   }
+  // timed calls: events attached to each kernel's own dispatch
   HIP_TRY(launch_resolve(h->view, s, layer, sel, ctx_len, out, sel_copy, multi_entries, app_rows,
-                         app_pos));
-  if (tc) HIP_TRY(hipEventRecord(tc->e1, s));
-  if (io && !h->view.fuse_fetch) {
-    HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x));
-    if (tc) HIP_TRY(hipEventRecord(tc->e2, s));
-  }
+                         app_pos, tc ? tc->e0 : nullptr, tc ? tc->e1 : nullptr));
+  if (io && !h->view.fuse_fetch)
+    HIP_TRY(launch_fetch(h->view, s, layer, h->fetch_grid_x, tc ? tc->e2 : nullptr,
+                         tc ? tc->e3 : nullptr));
   return HISPARSE_OK;
 }
 
@@ -204,6 +202,7 @@ void release(hisparse* h) {
     (void)hipEventDestroy(c.e0);
     (void)hipEventDestroy(c.e1);
     (void)hipEventDestroy(c.e2);
+    (void)hipEventDestroy(c.e3);
   }
   if (h->d_host) (void)hipFree(h->d_host);
   if (h->pf_out) (void)hipFree(h->pf_out);
@@ -663,7 +662,7 @@ int hisparse_set_timing(hisparse_t h, int enable) {
     h->pool.resize(n);
     for (auto& c : h->pool) {
       if (hipEventCreate(&c.e0) != hipSuccess || hipEventCreate(&c.e1) != hipSuccess ||
-          hipEventCreate(&c.e2) != hipSuccess)
+          hipEventCreate(&c.e2) != hipSuccess || hipEventCreate(&c.e3) != hipSuccess)
         return fail(HISPARSE_ERR_HIP, "timing event creation failed");
     }
   }

@@ -234,17 +234,18 @@ def test_prefetch_with_a_growing_context():
         a.close()
 
 
-@pytest.mark.parametrize("captured", [False, True])
-def test_prefetch_schedule_against_the_oracle(captured):
+@pytest.mark.parametrize("captured,k", [(False, 1500), (True, 1500), (False, 1001)])
+def test_prefetch_schedule_against_the_oracle(captured, k):
     """Shared selections, layer-wise prefetch: layer 0 resolved on the main
     stream, then every layer l+1 prefetched on a second stream and joined by
     its resolve.  Every step (eager, or one captured step replayed with
     eager copies in between) is compared with the oracle resolving every
     layer in order: slot maps, clocks, counters, eviction logs, LRU state,
-    position->slot tables and slot bytes of every stream."""
+    position->slot tables and slot bytes of every stream.  An odd k leaves
+    the rows unaligned for the join's 16-byte copies (its scalar path)."""
     torch, hb = _torch(), _hb()
     from tests.gpu_harness import LockstepRun
-    cfg = WORKLOADS[4].scaled(B=3, layers=4, L0=30000, C=3000, k=1500, steps=10)
+    cfg = WORKLOADS[4].scaled(B=3, layers=4, L0=30000, C=3000, k=k, steps=10)
     run = LockstepRun(cfg)
     try:
         main, side = torch.cuda.Stream(), torch.cuda.Stream()

@@ -38,6 +38,9 @@ CASES = {
     "k_one": (2, dict(B=2, L0=500, C=4, R=3, k=1, steps=20, carry_pct=0)),
     "largest_supported_shape": (1, dict(L0=60000, C=12000, k=3000, steps=4)),
     "window_covers_context": (3, dict(B=2, layers=1, L0=40, C=64, R=64, k=32, steps=12)),
+    # ten requests: a forced split fetch takes the flat fan-out kernel (below eight
+    # streams per call the grid is sliced per stream instead)
+    "many_requests": (2, dict(B=10, L0=8192, C=1500, k=700, steps=6)),
     # the context grows past the window (58 .. 69 rows, R = 64): the first steps are all
     # resident, then the oldest positions leave the window and are fetched when selected
     "window_boundary_crossing": (3, dict(B=2, layers=1, L0=58, C=64, R=64, k=24, steps=12)),
@@ -52,10 +55,11 @@ def test_parity_reduced(name):
 
 @pytest.mark.parametrize("mode", ["fused", "split"])
 @pytest.mark.parametrize("name", ["one_request_ragged", "independent_layers_growth", "pages",
-                                  "largest_supported_shape"])
+                                  "largest_supported_shape", "many_requests"])
 def test_parity_fetch_modes(name, mode, monkeypatch):
     """Both miss-fetch paths (copies by the resolve workgroups themselves, or
-    by a separate fan-out kernel) on the same cases."""
+    by a separate fan-out kernel: sliced per stream below eight streams per
+    call, flat above) on the same cases."""
     monkeypatch.setenv("HISPARSE_FETCH_MODE", mode)
     base, kw = CASES[name]
     _parity_case(name, base, kw)
