@@ -124,12 +124,13 @@ def host_mem_available_gib():
 class Setup:
     """Host histories, two library instances (IO and no-IO) and device inputs."""
 
-    def __init__(self, cfg, host_flags, queries=1, numa_node=-1, prefetch=False):
+    def __init__(self, cfg, host_flags, queries=1, numa_node=-1, prefetch=False, warmup=0):
         import torch
         from hierarchical_kv_cache_hisparse_amd import binding as hb
         from hierarchical_kv_cache_hisparse_amd.instance import GpuInstance, host_view
         from workload.prepare import appended_row, fill_host, make_trace
         self.torch, self.hb, self.cfg, self.queries = torch, hb, cfg, queries
+        self.W = warmup    # untimed decode steps before every timed region
         # the workload's layer-wise prefetch schedule (shared selections only)
         self.prefetch = bool(prefetch and cfg.shared_selection and cfg.layers > 1 and queries == 1)
         self.side = torch.cuda.Stream() if self.prefetch else None
@@ -187,6 +188,16 @@ class Setup:
         hb.hisparse_reset(inst.h, s, -1, -1)
         hb.hisparse_load_window(inst.h, s, -1, self.ctx[0].data_ptr())
         self.torch.cuda.synchronize()
+
+    def warm(self, inst):
+        """Reset `inst`, then run the W warm-up steps (0 .. W-1) eagerly: the
+        state every timed region starts from.  Returns the running totals
+        (misses, evictions, hits) after them."""
+        self.reset(inst)
+        for s in range(self.W):
+            self.step(inst, s)
+        self.torch.cuda.synchronize()
+        return self.totals(inst)
 
     def step(self, inst, s, stream=None):
         hb, cfg = self.hb, self.cfg
@@ -400,9 +411,16 @@ def summarize_rocprof(directory, label, command, tail=0):
     if pmc:
         agg = {}
         with open(pmc[0]) as f:
-            for row in csv.DictReader(f):
-                key = (short_kernel_name(row["Kernel_Name"]), row["Counter_Name"])
-                agg.setdefault(key, []).append(float(row["Counter_Value"]))
+            rows = list(csv.DictReader(f))
+        if rows and "Dispatch_Id" in rows[0]:
+            rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        for row in rows:
+            key = (short_kernel_name(row["Kernel_Name"]), row["Counter_Name"])
+            agg.setdefault(key, []).append(float(row["Counter_Value"]))
+        if tail:   # each kernel's last `tail` dispatches (e.g. the timed steps)
+            agg = {key: v[-tail:] for key, v in agg.items()}
+            lines += [f"PMC means over the last {tail} dispatches of each kernel "
+                      f"(all of them where it has fewer)", ""]
         lines += ["## PMC counters (per dispatch)", "",
                   "| kernel | counter | dispatches | mean per dispatch | total |",
                   "|---|---|---|---|---|"]
@@ -454,18 +472,23 @@ def committed_traffic(kernels, label, mode):
         cmd = cmd.group(1) if cmd else ""
         st = re.search(r"--steps (\d+)", cmd)
         wu = re.search(r"--warmup (\d+)", cmd)
+        tl = re.search(r"^PMC means over the last (\d+) dispatches", text, re.M)
         vals.setdefault("profiled", []).append({
             "counter": counter, "steps": int(st.group(1)) if st else None,
-            "warmup": int(wu.group(1)) if wu else None, "serial": "--serial" in cmd})
+            "warmup": int(wu.group(1)) if wu else None, "serial": "--serial" in cmd,
+            "tail": int(tl.group(1)) if tl else None})
     return vals
 
 
-def traffic_matches(t, K, serial):
-    """True when every counter run of `t` profiled exactly K steps with no
-    warm-up on the same schedule, i.e. its per-dispatch means are over the
-    launches whose algorithmic bytes this run computes."""
-    return bool(t) and all(p["steps"] == K and p["warmup"] == 0 and p["serial"] == serial
-                           for p in t["profiled"])
+def traffic_matches(t, K, W, launches, serial):
+    """True when every counter run of `t` profiled the same K timed steps
+    after the same W warm-up steps on the same schedule, and its
+    per-dispatch means are over exactly those steps' `launches` launches
+    (the whole run when there is no warm-up)."""
+    return bool(t) and all(
+        p["steps"] == K and p["warmup"] == W and p["serial"] == serial
+        and (p["tail"] == launches or (W == 0 and p["tail"] is None))
+        for p in t["profiled"])
 
 
 def traffic_fields(t):
@@ -534,18 +557,19 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
                 hb.hisparse_resolve(inst.h, ms, setup.sel[s, l + 1].data_ptr(),
                                     setup.ctx[s].data_ptr(), l + 1, setup.out[l + 1].data_ptr())
 
+    W = setup.W
+
     def timed(inst, schedule):
-        setup.reset(inst)
         main, side = torch.cuda.Stream(), torch.cuda.Stream()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(main):
             with torch.cuda.graph(g, stream=main):
-                for s in range(K):
+                for s in range(W, W + K):
                     schedule(inst, s, main.cuda_stream, side.cuda_stream)
         torch.cuda.synchronize()
         best = None
         for _ in range(2):
-            setup.reset(inst)
+            setup.warm(inst)
             t0 = time.perf_counter()
             g.replay()
             torch.cuda.synchronize()
@@ -568,7 +592,8 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
                             "no_io": round(t_noio / K * 1e3, 4)},
             "miss_overhead_us_per_step": {"serial": round((t_serial - t_noio) / K * 1e6, 1),
                                           "prefetch": round((t_pref - t_noio) / K * 1e6, 1)},
-            "mode": "one HIP graph per schedule, best of 2 replays from a cold cache"}
+            "mode": f"one HIP graph per schedule of steps {W} .. {W + K - 1}, best of 2 replays "
+                    f"after the {W} warm-up steps"}
 
 
 def _mla_cpu_baseline(setup, K, q_np, rows, Q, per, scale):
@@ -750,16 +775,16 @@ def topk_study(cfg, K, W):
                              "sample": f"numpy lexsort oracle on {n_cpu} of {B} rows, scaled"}}
 
 
-def capture_steps(setup, inst, K):
-    """All K steps of `inst` captured into one HIP graph (on a side stream);
-    the instance is reset first."""
+def capture_steps(setup, inst, K, first=0):
+    """Steps first .. first+K-1 of `inst` captured into one HIP graph (on a
+    side stream); capturing runs nothing, so the caller sets the state each
+    replay starts from (setup.warm, or setup.reset for first = 0)."""
     import torch
-    setup.reset(inst)
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            for s in range(K):
+            for s in range(first, first + K):
                 setup.step(inst, s)
     torch.cuda.synchronize()
     return g
@@ -851,8 +876,9 @@ def pipeline_study(setup, K, H):
 
 
 def cpu_baseline(setup, steps, threads=1, min_seconds=10.0, no_io_seconds=0.0):
-    """The CPU oracle (plain C) on the same trace and host rows, repeated from
-    a cold state until at least `min_seconds` of wall time are measured.  With
+    """The CPU oracle (plain C) on the same trace and host rows: the timed
+    steps W .. W+steps-1 after the W untimed warm-up steps (setup.W, 0 if
+    absent), repeated until at least `min_seconds` of wall time are measured.  With
     threads > 1 the independent streams are spread over that many threads
     (the C oracle runs without the Python lock).  With no_io_seconds > 0 the
     same trace is also timed with the row copies suppressed, and the copy rate
@@ -864,10 +890,20 @@ def cpu_baseline(setup, steps, threads=1, min_seconds=10.0, no_io_seconds=0.0):
     host_of = lambda b, l: setup.hosts[(b, l)][1]
     groups = [streams[i::threads] for i in range(threads)]
 
-    def run_group(group, no_io):
+    W = getattr(setup, "W", 0)
+
+    def warm_group(group, no_io):
+        """Oracle streams after the W warm-up steps (untimed)."""
         run = OracleRun(cfg, group, host_of=host_of)
+        for s in range(W):
+            if cfg.growth and s > 0:
+                run.append(s)
+            run.step(s, setup.trace, no_io=no_io, queries=setup.queries)
+        return run
+
+    def run_group(run, no_io):
         missed = 0
-        for s in range(steps):
+        for s in range(W, W + steps):
             if cfg.growth and s > 0:
                 run.append(s)
             res = run.step(s, setup.trace, no_io=no_io, queries=setup.queries)
@@ -878,8 +914,9 @@ def cpu_baseline(setup, steps, threads=1, min_seconds=10.0, no_io_seconds=0.0):
         elapsed, entries, reps, missed = 0.0, 0, 0, 0
         with ThreadPoolExecutor(threads) as pool:
             while elapsed < seconds and reps < 2000:
+                runs = list(pool.map(lambda g: warm_group(g, no_io), groups))
                 t0 = time.perf_counter()
-                missed += sum(pool.map(lambda g: run_group(g, no_io), groups))
+                missed += sum(pool.map(lambda r: run_group(r, no_io), runs))
                 elapsed += time.perf_counter() - t0
                 entries += steps * cfg.layers * cfg.B * cfg.k
                 reps += 1
@@ -887,13 +924,14 @@ def cpu_baseline(setup, steps, threads=1, min_seconds=10.0, no_io_seconds=0.0):
 
     elapsed, entries, reps, missed = timed(False, min_seconds)
     out = {"value": entries / elapsed, "unit": "entries/s", "cores": threads, "kind": "oracle",
-           "sample": f"{reps} x the full {steps}-step trace of all {len(streams)} streams "
-                     f"with row copies ({elapsed:.1f}s wall, {threads} thread(s))",
+           "sample": f"{reps} x steps {W} .. {W + steps - 1} of the trace (after {W} untimed "
+                     f"warm-up steps) on all {len(streams)} streams with row copies "
+                     f"({elapsed:.1f}s wall, {threads} thread(s))",
            "cpu_model": cpu_model()}
     if no_io_seconds > 0:
         e2, n2, r2, _ = timed(True, no_io_seconds)
         out["no_io_value"] = n2 / e2
-        out["no_io_sample"] = f"{r2} x the same trace, row copies suppressed ({e2:.1f}s wall)"
+        out["no_io_sample"] = f"{r2} x the same steps, row copies suppressed ({e2:.1f}s wall)"
         copy_s = elapsed / reps - e2 / r2
         out["memcpy_GBps"] = (round(missed / reps * cfg.row_bytes / copy_s / 1e9, 3)
                               if copy_s > 0 else None)
@@ -936,13 +974,14 @@ def main():
             calibration_copy()
         print(json.dumps(result), flush=True)
         return
-    S = max(args.steps, args.warmup, 1)
+    S = max(args.warmup + args.steps, 1)   # warm-up steps, then the timed ones
     Q = max(1, args.queries)
     cfg = base.scaled(steps=S) if S != base.steps else base
     if Q > 1:   # Q query tokens, each with the workload's k selections
         cfg = cfg.scaled(k=Q * base.k)
     host_flags = hb.HISPARSE_HOST_NONCOHERENT if args.host_noncoherent else hb.HISPARSE_HOST_COHERENT
-    setup = Setup(cfg, host_flags, queries=Q, numa_node=args.numa_node, prefetch=not args.serial)
+    setup = Setup(cfg, host_flags, queries=Q, numa_node=args.numa_node, prefetch=not args.serial,
+                  warmup=args.warmup)
     K, W = args.steps, args.warmup
     io = setup.noio if (args.no_io and args.only_timed) else setup.io
     if args.pipeline:
@@ -968,45 +1007,45 @@ def main():
             setup.close()
         return
     try:
-        # ---- warm-up, then a kernel-timing pass from a cold cache: eager
-        # launches with the library's HIP events on the launch stream (events
+        # ---- the W warm-up steps (0 .. W-1, the cold fill among them), then
+        # a kernel-timing pass over steps W .. W+K-1: eager launches with the
+        # library's timing events attached to each kernel's dispatch (events
         # cannot be recorded inside a captured graph) --------------------------
-        for s in range(W):
-            setup.step(io, s)
-        torch.cuda.synchronize()
-        setup.reset(io)
+        base_tot = setup.warm(io)
         hb.hisparse_set_timing(io.h, True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(K):
+        for s in range(W, W + K):
             setup.step(io, s)
         torch.cuda.synchronize()
         elapsed_eager = time.perf_counter() - t0
         timing = hb.hisparse_get_timing(io.h)
         hb.hisparse_set_timing(io.h, False)
-        tot_miss, tot_evict, tot_hit = (int(x) for x in setup.totals(io))
+        end_tot = setup.totals(io)
+        tot_miss, tot_evict, tot_hit = (int(x) for x in end_tot - base_tot)
         assert io.status() == 0, "device status word set during the benchmark"
         entries = K * cfg.layers * cfg.B * cfg.k
         miss_bytes = tot_miss * cfg.row_bytes
-        log(f"eager: {K} steps in {elapsed_eager * 1e3:.2f} ms; misses {tot_miss}, evictions "
-            f"{tot_evict}, hits {tot_hit}; kernel time resolve {timing['resolve_ms']:.3f} ms / "
-            f"{timing['resolve_launches']}, fetch {timing['fetch_ms']:.3f} ms / "
-            f"{timing['fetch_launches']}")
+        log(f"eager: {K} steps after {W} warm-up steps in {elapsed_eager * 1e3:.2f} ms; misses "
+            f"{tot_miss}, evictions {tot_evict}, hits {tot_hit}; kernel time resolve "
+            f"{timing['resolve_ms']:.3f} ms / {timing['resolve_launches']}, fetch "
+            f"{timing['fetch_ms']:.3f} ms / {timing['fetch_launches']}")
 
-        # ---- the timed region: all K steps (every layer's call) captured as
-        # one HIP graph, as a decode graph holds them, replayed once from a
-        # cold cache after one warm replay ------------------------------------
+        # ---- the timed region: steps W .. W+K-1 (every layer's call) captured
+        # as one HIP graph, as a decode graph holds them, replayed once after
+        # the warm-up steps (and after one untimed replay) ---------------------
         graph_ev_ms = None
         if args.only_timed and not args.with_graph:
             elapsed = elapsed_eager
-            mode = "eager, library HIP-event timing on"
+            mode = "eager, library kernel timing on"
         else:
-            graph = capture_steps(setup, io, K)
+            graph = capture_steps(setup, io, K, first=W)
+            setup.warm(io)
             graph.replay()
             torch.cuda.synchronize()
-            setup.reset(io)
+            setup.warm(io)
             # HIP events on the stream the graph is launched on, around the
-            # timed replay: its nodes are the K steps' resolve launches
+            # timed replay
             ev0 = torch.cuda.Event(enable_timing=True)
             ev1 = torch.cuda.Event(enable_timing=True)
             t0 = time.perf_counter()
@@ -1017,12 +1056,13 @@ def main():
             elapsed = time.perf_counter() - t0
             graph_ev_ms = ev0.elapsed_time(ev1)
             assert io.status() == 0, "device status word set during the benchmark"
-            assert tuple(int(x) for x in setup.totals(io)) == (tot_miss, tot_evict, tot_hit), \
+            assert tuple(int(x) for x in setup.totals(io)) == tuple(int(x) for x in end_tot), \
                 "graph replay and eager pass disagree"
             del graph
-            mode = "one HIP graph of all K steps, one timed replay from a cold cache" + (
-                "; every layer l+1 prefetched on a second stream (forked after layer l) and "
-                "joined by its resolve" if setup.prefetch else "")
+            mode = (f"one HIP graph of steps {W} .. {W + K - 1}, one timed replay after the "
+                    f"{W} warm-up steps" + (
+                        "; every layer l+1 prefetched on a second stream (forked after layer l) "
+                        "and joined by its resolve" if setup.prefetch else ""))
             log(f"timed: {K} steps in {elapsed * 1e3:.3f} ms (graph replay)")
         value = entries / elapsed
 
@@ -1061,9 +1101,11 @@ def main():
         # counters are reported only when taken over the same K steps (from a
         # cold cache, no warm-up) and schedule as this run
         traffic_note = None
-        if traffic and not traffic_matches(traffic, K, not setup.prefetch):
-            traffic_note = (f"counter summaries were taken over another step count or schedule "
-                            f"({traffic['profiled']}); this run has {K} steps")
+        n_launch = K * cfg.layers
+        if traffic and not traffic_matches(traffic, K, W, n_launch, not setup.prefetch):
+            traffic_note = (f"counter summaries were taken over other steps or another schedule "
+                            f"({traffic['profiled']}); this run times {K} steps after {W} "
+                            f"warm-up steps")
             traffic = None
 
         result = {
@@ -1084,6 +1126,8 @@ def main():
                        "resident_window": cfg.R, "top_k": cfg.k, "steps": K,
                        "carry_over_pct": cfg.carry_pct, "replacement": cfg.replacement,
                        "shared_selection": cfg.shared_selection,
+                       "timed_steps": f"{W} .. {W + K - 1}, after {W} untimed warm-up steps "
+                                      f"(step 0, the cold fill, among them)",
                        "schedule": "layer-wise prefetch" if setup.prefetch else "serial",
                        "timed_launch_mode": mode},
             "roofline": {"bound": "host_link", "kernel": dominant, "fused_fetch": fused,
@@ -1107,8 +1151,9 @@ def main():
                          "traffic_source": (
                              f"rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE summaries "
                              f"profiles/pmc_{{fetch,write}}_size_{cfg.label}_"
-                             f"{'fused' if fused else 'split'}.md, {K} steps from a cold cache, "
-                             f"scaled by the 256 MiB device copy" if traffic else traffic_note),
+                             f"{'fused' if fused else 'split'}.md, the same {K} steps after {W} "
+                             f"warm-up steps, scaled by the 256 MiB device copy"
+                             if traffic else traffic_note),
                          "avg_launch_us": round(fetch_avg_s * 1e6, 3),
                          "launch_timing": launch_timing,
                          "avg_launch_us_eager": round(
@@ -1145,14 +1190,15 @@ def main():
         if not args.only_timed:
             # ---- graph replay, best of 3 (IO and no-IO) --------------------
             def graph_pass(inst):
-                """All K steps in one HIP graph, replayed from a cold cache:
-                best wall time and best HIP-event time (ms) of 3 replays."""
-                g = capture_steps(setup, inst, K)
-                g.replay()                      # warm replay
+                """Steps W .. W+K-1 in one HIP graph, replayed after the warm-up
+                steps: best wall time and best HIP-event time (ms) of 3 replays."""
+                g = capture_steps(setup, inst, K, first=W)
+                setup.warm(inst)
+                g.replay()                      # untimed replay
                 torch.cuda.synchronize()
                 best, best_ev = None, None
                 for _ in range(3):
-                    setup.reset(inst)
+                    setup.warm(inst)
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     t0 = time.perf_counter()
@@ -1170,9 +1216,9 @@ def main():
             dt_io, _ = graph_pass(io)
             dt_noio, ev_noio_ms = graph_pass(setup.noio)
             # resolve kernel alone, copies suppressed: eager launches, HIP events
-            setup.reset(setup.noio)
+            setup.warm(setup.noio)
             hb.hisparse_set_timing(setup.noio.h, True)
-            for s in range(K):
+            for s in range(W, W + K):
                 setup.step(setup.noio, s)
             t_noio = hb.hisparse_get_timing(setup.noio.h)
             hb.hisparse_set_timing(setup.noio.h, False)
@@ -1193,7 +1239,7 @@ def main():
             rk["achieved"] = round(meta_bytes / (rk_us * 1e-6) / 1e9, 3)
             rk["frac"] = round(rk["achieved"] / HBM_PEAK_GBPS, 6)
             t_meta = committed_traffic("resolve_kernel", cfg.label, "noio")
-            if t_meta and not traffic_matches(t_meta, K, not setup.prefetch):
+            if t_meta and not traffic_matches(t_meta, K, W, K * cfg.layers, not setup.prefetch):
                 t_meta = None
             rk["traffic"] = round(t_meta["FETCH_SIZE"] + t_meta["WRITE_SIZE"]) if t_meta else None
             rk["traffic_read_bytes"] = round(t_meta["FETCH_SIZE"]) if t_meta else None
@@ -1220,6 +1266,7 @@ def main():
             result["no_io"]["step_budget_us"] = NOIO_STEP_BUDGET_US
             # ---- step 0 alone (the cold fill: about k misses per stream) ----
             def cold_step(inst):
+                setup.reset(inst)
                 g = capture_steps(setup, inst, 1)
                 g.replay()
                 torch.cuda.synchronize()

@@ -32,8 +32,11 @@ def test_committed_traffic_is_current(mode):
     times, and the scaled byte counts are of the size the workload implies."""
     t = bench.committed_traffic("resolve_kernel", "tokens_b16x8_L256k", mode)
     assert t is not None, "PMC summaries missing or taken on other kernel sources"
-    assert bench.traffic_matches(t, 20, serial=False)
-    assert not bench.traffic_matches(t, 32, serial=False)
+    # the driver's run: 20 timed steps x 8 layers after 5 warm-up steps
+    assert bench.traffic_matches(t, 20, 5, 160, serial=False)
+    assert not bench.traffic_matches(t, 32, 5, 256, serial=False)
+    assert not bench.traffic_matches(t, 20, 0, 160, serial=False)
+    assert not bench.traffic_matches(t, 20, 5, 160, serial=True)
     # per launch: 16 streams x 2048 selections of metadata at least; with the
     # copies, about 9.4 MB of miss rows read and written on average
     assert t["FETCH_SIZE"] > 16 * 2048 * 4 and t["WRITE_SIZE"] > 16 * 2048 * 4
@@ -67,14 +70,14 @@ def test_summary_writer_round_trip(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
     d = tmp_path / "raw" / "node"
     d.mkdir(parents=True)
-    rows = ["Kernel_Name,Counter_Name,Counter_Value"]
-    rows += ["hsp::resolve_kernel<4>(args),FETCH_SIZE,100.0",
-             "hsp::resolve_kernel<4>(args),FETCH_SIZE,300.0",
-             "hsp::probe_host_read_kernel(args),FETCH_SIZE,131072.0"]
+    rows = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+    rows += ["1,hsp::resolve_kernel<4>(args),FETCH_SIZE,100.0",
+             "2,hsp::resolve_kernel<4>(args),FETCH_SIZE,300.0",
+             "3,hsp::probe_host_read_kernel(args),FETCH_SIZE,131072.0"]
     (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
     bench.summarize_rocprof(str(tmp_path / "raw"), "pmc_fetch_size_x_fused", "cmd")
     rows[1:] = [r.replace("FETCH_SIZE", "WRITE_SIZE") for r in rows[1:]]
-    rows[-1] = "hsp::probe_host_read_kernel(args),WRITE_SIZE,262144.0"
+    rows[-1] = "3,hsp::probe_host_read_kernel(args),WRITE_SIZE,262144.0"
     (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
     bench.summarize_rocprof(str(tmp_path / "raw"), "pmc_write_size_x_fused", "cmd")
     t = bench.committed_traffic("resolve_kernel", "x", "fused")
@@ -83,6 +86,18 @@ def test_summary_writer_round_trip(tmp_path, monkeypatch):
     assert t["WRITE_SIZE"] == pytest.approx(200 * 1024 * 1.0)
     text = (tmp_path / "profiles" / "pmc_fetch_size_x_fused.md").read_text()
     assert "Command: `cmd`" in text and "| resolve_kernel | FETCH_SIZE | 2 | 200.0 | 400.0 |" in text
+    # with a tail, the means cover each kernel's last dispatches only
+    bench.summarize_rocprof(str(tmp_path / "raw"), "pmc_write_size_x_fused",
+                            "bench.py --steps 1 --warmup 1", tail=1)
+    rows[1:] = [r.replace("WRITE_SIZE", "FETCH_SIZE") for r in rows[1:]]
+    rows[-1] = "3,hsp::probe_host_read_kernel(args),FETCH_SIZE,131072.0"
+    (d / "run_counter_collection.csv").write_text("\n".join(rows) + "\n")
+    bench.summarize_rocprof(str(tmp_path / "raw"), "pmc_fetch_size_x_fused",
+                            "bench.py --steps 1 --warmup 1", tail=1)
+    t = bench.committed_traffic("resolve_kernel", "x", "fused")
+    assert t["FETCH_SIZE"] == pytest.approx(300 * 1024 * 2.0)   # the last dispatch only
+    assert bench.traffic_matches(t, 1, 1, 1, serial=False)
+    assert not bench.traffic_matches(t, 1, 1, 2, serial=False)
 
 
 def test_cpu_baseline_runs_the_oracle():
@@ -93,11 +108,11 @@ def test_cpu_baseline_runs_the_oracle():
     hosts = {(b, l): (None, np.zeros((cfg.l_cap, cfg.row_bytes), np.uint8))
              for b in range(cfg.B) for l in range(cfg.layers)}
     fill_host(cfg, lambda b, l: hosts[(b, l)][1], trace, list(hosts))
-    setup = types.SimpleNamespace(cfg=cfg, trace=trace, hosts=hosts, queries=1)
-    r = bench.cpu_baseline(setup, cfg.steps, threads=2, min_seconds=0.2, no_io_seconds=0.1)
+    setup = types.SimpleNamespace(cfg=cfg, trace=trace, hosts=hosts, queries=1, W=1)
+    r = bench.cpu_baseline(setup, cfg.steps - 1, threads=2, min_seconds=0.2, no_io_seconds=0.1)
     assert r["kind"] == "oracle" and r["cores"] == 2 and r["unit"] == "entries/s"
     assert r["value"] > 0 and r["no_io_value"] > 0
-    assert "trace of all 2 streams" in r["sample"]
+    assert "steps 1 .. 2 of the trace (after 1 untimed warm-up steps) on all 2 streams" in r["sample"]
 
 
 def test_only_the_cpu_baseline_legs_reach_the_oracle():
