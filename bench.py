@@ -211,7 +211,8 @@ class Setup:
                                 self.out[0].data_ptr())
             for l in range(cfg.layers - 1):
                 hb.hisparse_prefetch(inst.h, st, self.side.cuda_stream,
-                                     self.sel[s, l + 1].data_ptr(), ctx, l + 1)
+                                     self.sel[s, l + 1].data_ptr(), ctx, l + 1,
+                                     self.out[l + 1].data_ptr())
                 hb.hisparse_resolve(inst.h, st, self.sel[s, l + 1].data_ptr(), ctx, l + 1,
                                     self.out[l + 1].data_ptr())
             return
@@ -551,7 +552,7 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
         for l in range(cfg.layers):
             if l + 1 < cfg.layers:
                 hb.hisparse_prefetch(inst.h, ms, ss, setup.sel[s, l + 1].data_ptr(),
-                                     setup.ctx[s].data_ptr(), l + 1)
+                                     setup.ctx[s].data_ptr(), l + 1, setup.out[l + 1].data_ptr())
             layer_compute(inst, l, ms)
             if l + 1 < cfg.layers:
                 hb.hisparse_resolve(inst.h, ms, setup.sel[s, l + 1].data_ptr(),

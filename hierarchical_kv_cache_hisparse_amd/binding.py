@@ -107,7 +107,7 @@ def library():
             "hisparse_destroy": [P],
             "hisparse_resolve": [P, P, P, P, I32, P],
             "hisparse_resolve_multi": [P, P, P, I32, I32, P, I32, P],
-            "hisparse_prefetch": [P, P, P, P, P, I32],
+            "hisparse_prefetch": [P, P, P, P, P, I32, P],
             "hisparse_load_window": [P, P, I32, P],
             "hisparse_append": [P, P, I32, P, P],
             "hisparse_append_resolve": [P, P, I32, P, P, P, P, P],
@@ -215,8 +215,9 @@ def hisparse_resolve_multi(h, stream: int, sel: int, queries: int, per_query: in
 
 
 def hisparse_prefetch(h, main_stream: int, side_stream: int, sel: int, ctx_len: int,
-                      layer: int) -> None:
-    _check(library().hisparse_prefetch(h, main_stream, side_stream, sel, ctx_len, layer),
+                      layer: int, out_slot: int = 0) -> None:
+    _check(library().hisparse_prefetch(h, main_stream, side_stream, sel, ctx_len, layer,
+                                       out_slot or None),
            "hisparse_prefetch")
 
 

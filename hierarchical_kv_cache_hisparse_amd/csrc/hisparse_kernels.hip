@@ -756,7 +756,8 @@ __global__ void append_kernel(StreamView v, int layer, const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Prefetch join: copy the prefetched slot map, check the selections match.
+// Prefetch join: copy the prefetched slot map (unless it was written to the
+// joining call's own buffer), check the selections match.
 // One load round trip: every thread handles kJoinItems consecutive entries of
 // one request row (4 consecutive int32 per load when the row allows it).
 // grid = (ceil(k / (256 * kJoinItems)), B)
@@ -766,8 +767,7 @@ constexpr int kJoinItems = 4;
 __global__ void __launch_bounds__(256)
     prefetch_join_kernel(StreamView v, const int32_t* __restrict__ sel,
                          const int32_t* __restrict__ sel_copy,
-                         const int32_t* __restrict__ pf_out, int32_t* __restrict__ out,
-                         int vec) {
+                         const int32_t* pf_out, int32_t* out, int vec) {
   const int64_t base = (int64_t)blockIdx.y * v.k;
   const int i0 = (blockIdx.x * 256 + threadIdx.x) * kJoinItems;
   int mismatch = 0;
@@ -776,14 +776,14 @@ __global__ void __launch_bounds__(256)
     const int4 c = *reinterpret_cast<const int4*>(sel_copy + base + i0);
     const int4 o = *reinterpret_cast<const int4*>(pf_out + base + i0);
     mismatch = (a.x != c.x) | (a.y != c.y) | (a.z != c.z) | (a.w != c.w);
-    *reinterpret_cast<int4*>(out + base + i0) = o;
+    if (pf_out != out) *reinterpret_cast<int4*>(out + base + i0) = o;
   } else {
 #pragma unroll
     for (int u = 0; u < kJoinItems; ++u) {
       const int i = i0 + u;
       if (i < v.k) {
         mismatch |= sel[base + i] != sel_copy[base + i];
-        out[base + i] = pf_out[base + i];
+        if (pf_out != out) out[base + i] = pf_out[base + i];
       }
     }
   }

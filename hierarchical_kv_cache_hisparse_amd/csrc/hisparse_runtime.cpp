@@ -131,6 +131,8 @@ struct hisparse {
   int32_t* pf_out = nullptr;     // [L][B][k] prefetched slot maps
   int32_t* pf_sel = nullptr;     // [L][B][k] prefetched selections
   std::vector<uint8_t> pending;  // per layer: a prefetch waits to be joined
+  std::vector<int32_t*> pf_dst;      // per layer: where the pending prefetch writes its map
+  std::vector<const int32_t*> pf_src;  // per layer: the selections it was given
   std::vector<hipEvent_t> ev_fork, ev_done;
   int fetch_grid_x = 64;  // fetch kernel workgroups
   size_t lds_max = 0;     // LDS bytes per workgroup of the device
@@ -435,6 +437,8 @@ int hisparse_create(const hisparse_config* cfg, void* const* host_rows, void* de
     return rc2;
   }
   h->pending.assign(L, 0);
+  h->pf_dst.assign(L, nullptr);
+  h->pf_src.assign(L, nullptr);
   h->ev_fork.assign(L, nullptr);
   h->ev_done.assign(L, nullptr);
   const size_t map_bytes = sizeof(int32_t) * (size_t)L * B * cfg->top_k;
@@ -522,11 +526,17 @@ int hisparse_resolve(hisparse_t h, hipStream_t stream, const int32_t* sel, const
                                 out_slot))
     return rc;
   if (h->pending[layer]) {
-    // join the prefetch: wait for it, then hand over its slot map
+    // join the prefetch: wait for it; when it wrote this very map from these
+    // very selections, that is all; otherwise a kernel copies its map here
+    // and compares the selections with the ones it resolved
     HIP_TRY(hipStreamWaitEvent(stream, h->ev_done[layer], 0));
-    const size_t off = (size_t)layer * h->cfg.num_requests * h->cfg.top_k;
-    HIP_TRY(launch_prefetch_join(h->view, stream, sel, h->pf_sel + off, h->pf_out + off,
-                                 out_slot));
+    const bool same = out_slot == h->pf_dst[layer] && sel == h->pf_src[layer] &&
+                      !(h->cfg.flags & HISPARSE_DEBUG_VALIDATE);
+    if (!same) {
+      const size_t off = (size_t)layer * h->cfg.num_requests * h->cfg.top_k;
+      HIP_TRY(launch_prefetch_join(h->view, stream, sel, h->pf_sel + off, h->pf_dst[layer],
+                                   out_slot));
+    }
     h->pending[layer] = 0;
     return HISPARSE_OK;
   }
@@ -542,13 +552,19 @@ int hisparse_resolve_multi(hisparse_t h, hipStream_t stream, const int32_t* sel,
 }
 
 int hisparse_prefetch(hisparse_t h, hipStream_t main_stream, hipStream_t side_stream,
-                      const int32_t* sel, const int32_t* ctx_len, int32_t layer) {
+                      const int32_t* sel, const int32_t* ctx_len, int32_t layer,
+                      int32_t* out_slot) {
   if (!h) return fail(HISPARSE_ERR_INVALID_ARG, "handle is NULL");
   if (!sel || !ctx_len) return fail(HISPARSE_ERR_INVALID_ARG, "sel and ctx_len must not be NULL");
   if (layer < 0 || layer >= h->cfg.num_layers)
     return fail(HISPARSE_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, h->cfg.num_layers);
   if (h->pending[layer])
     return fail(HISPARSE_ERR_STATE, "layer %d already has a pending prefetch", layer);
+  if (out_slot) {
+    if (int rc = check_no_overlap(h, sel, (size_t)h->cfg.num_requests * h->cfg.top_k, ctx_len,
+                                  out_slot))
+      return rc;
+  }
   const bool serial = (h->cfg.flags & HISPARSE_SERIALIZE_PREFETCH) || side_stream == main_stream;
   hipStream_t s = serial ? main_stream : side_stream;
   if (!serial) {
@@ -556,10 +572,13 @@ int hisparse_prefetch(hisparse_t h, hipStream_t main_stream, hipStream_t side_st
     HIP_TRY(hipStreamWaitEvent(side_stream, h->ev_fork[layer], 0));
   }
   const size_t off = (size_t)layer * h->cfg.num_requests * h->cfg.top_k;
-  int rc = enqueue_resolve(h, s, sel, ctx_len, layer, h->pf_out + off, h->pf_sel + off);
+  int32_t* dst = out_slot ? out_slot : h->pf_out + off;
+  int rc = enqueue_resolve(h, s, sel, ctx_len, layer, dst, h->pf_sel + off);
   if (rc) return rc;
   HIP_TRY(hipEventRecord(h->ev_done[layer], s));
   h->pending[layer] = 1;
+  h->pf_dst[layer] = dst;
+  h->pf_src[layer] = sel;
   return HISPARSE_OK;
 }
 

@@ -247,16 +247,25 @@ int hisparse_resolve_multi(hisparse_t h, hipStream_t stream, const int32_t* sel,
  * enqueued on `main_stream` (event fork), for models whose layers share one
  * selection.  The next hisparse_resolve of that layer on `main_stream` joins
  * it (event wait) and returns the same slot map; the state after prefetch +
- * resolve equals the state after the resolve alone.  The resolve must pass
- * the same selections: a difference sets HISPARSE_STATUS_PREFETCH_MISMATCH.
+ * resolve equals the state after the resolve alone.
+ *   out_slot: NULL, or the buffer the joining resolve will pass, [B, k]: the
+ *             prefetch writes the slot map there directly (on the side
+ *             stream: no other work may read or write it until the join).
+ * The resolve must pass the same selections.  When it passes the same sel
+ * and out_slot pointers as the prefetch (and HISPARSE_DEBUG_VALIDATE is
+ * off), the join is only an event wait: the selections' contents are taken
+ * as unchanged.  Otherwise a join kernel copies the prefetched map into its
+ * out_slot and compares the selections with the prefetched ones: a
+ * difference sets HISPARSE_STATUS_PREFETCH_MISMATCH.
  * [P3 Abstract: exact layer-wise prefetching for models sharing selections
  * across layers; P3 AI Summary: per-layer prefetching hides part of the miss
  * penalty; P1 Timeline: not applicable to layers with independent
  * selections.]
- * Errors: INVALID_ARG, STATE (the layer already has a pending prefetch),
- * HIP. */
+ * Errors: INVALID_ARG (also out_slot overlapping sel or ctx_len), STATE (the
+ * layer already has a pending prefetch), HIP. */
 int hisparse_prefetch(hisparse_t h, hipStream_t main_stream, hipStream_t side_stream,
-                      const int32_t* sel, const int32_t* ctx_len, int32_t layer);
+                      const int32_t* sel, const int32_t* ctx_len, int32_t layer,
+                      int32_t* out_slot);
 
 /* Copy the rows of positions [max(0, ctx-R), ctx) of every request from the
  * host history into their resident ring slots C + (p mod R) of `layer`

@@ -95,19 +95,24 @@ class LockstepRun:
                 hb.hisparse_resolve(self.gpu.h, self.gpu.stream, self.sel_dev[s, l].data_ptr(),
                                     self.ctx_dev[s].data_ptr(), l, self.out_dev[l].data_ptr())
 
-    def prefetch_step(self, s: int, main: int, side: int, sel=None, ctx=None, out=None):
+    def prefetch_step(self, s: int, main: int, side: int, sel=None, ctx=None, out=None,
+                      direct=True):
         """Step s with the layer-wise prefetch schedule of shared selections:
         resolve layer 0 on `main`; then for every layer l, prefetch layer l+1
         on `side` (forked from `main` after layer l's call) and resolve layer
         l+1 on `main`, which joins the prefetch.  sel / ctx / out default to
-        this run's buffers for step s (a graph passes fixed buffers)."""
+        this run's buffers for step s (a graph passes fixed buffers).  direct:
+        the prefetch writes the layer's slot-map buffer itself (the join is an
+        event wait); else it writes the library's own buffer and the join
+        copies it."""
         sel = self.sel_dev[s] if sel is None else sel
         ctx = self.ctx_dev[s] if ctx is None else ctx
         out = self.out_dev if out is None else out
         h = self.gpu.h
         hb.hisparse_resolve(h, main, sel[0].data_ptr(), ctx.data_ptr(), 0, out[0].data_ptr())
         for l in range(self.cfg.layers - 1):
-            hb.hisparse_prefetch(h, main, side, sel[l + 1].data_ptr(), ctx.data_ptr(), l + 1)
+            hb.hisparse_prefetch(h, main, side, sel[l + 1].data_ptr(), ctx.data_ptr(), l + 1,
+                                 out[l + 1].data_ptr() if direct else 0)
             hb.hisparse_resolve(h, main, sel[l + 1].data_ptr(), ctx.data_ptr(), l + 1,
                                 out[l + 1].data_ptr())
 

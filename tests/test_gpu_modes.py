@@ -234,15 +234,18 @@ def test_prefetch_with_a_growing_context():
         a.close()
 
 
-@pytest.mark.parametrize("captured,k", [(False, 1500), (True, 1500), (False, 1001)])
-def test_prefetch_schedule_against_the_oracle(captured, k):
+@pytest.mark.parametrize("captured,k,direct", [(False, 1500, True), (True, 1500, True),
+                                                (False, 1001, False), (True, 1500, False)])
+def test_prefetch_schedule_against_the_oracle(captured, k, direct):
     """Shared selections, layer-wise prefetch: layer 0 resolved on the main
     stream, then every layer l+1 prefetched on a second stream and joined by
     its resolve.  Every step (eager, or one captured step replayed with
     eager copies in between) is compared with the oracle resolving every
     layer in order: slot maps, clocks, counters, eviction logs, LRU state,
-    position->slot tables and slot bytes of every stream.  An odd k leaves
-    the rows unaligned for the join's 16-byte copies (its scalar path)."""
+    position->slot tables and slot bytes of every stream.  direct: the
+    prefetch writes the slot-map buffer the join passes (the join is an event
+    wait), else the library's own buffer (the join copies it; an odd k leaves
+    the rows unaligned for its 16-byte copies, the scalar path)."""
     torch, hb = _torch(), _hb()
     from tests.gpu_harness import LockstepRun
     cfg = WORKLOADS[4].scaled(B=3, layers=4, L0=30000, C=3000, k=k, steps=10)
@@ -258,7 +261,7 @@ def test_prefetch_schedule_against_the_oracle(captured, k):
             with torch.cuda.stream(main):
                 with torch.cuda.graph(graph, stream=main):
                     run.prefetch_step(0, main.cuda_stream, side.cuda_stream, sel=sel_buf,
-                                      ctx=ctx_buf)
+                                      ctx=ctx_buf, direct=direct)
             torch.cuda.synchronize()
         for s in range(cfg.steps):
             if captured:
@@ -268,7 +271,7 @@ def test_prefetch_schedule_against_the_oracle(captured, k):
                 graph.replay()
             else:
                 torch.cuda.synchronize()
-                run.prefetch_step(s, main.cuda_stream, side.cuda_stream)
+                run.prefetch_step(s, main.cuda_stream, side.cuda_stream, direct=direct)
             torch.cuda.synchronize()
             run.compare_step(s, run.oracle_step(s))
         assert run.gpu.status() == 0
@@ -378,6 +381,63 @@ def test_prefetch_misuse_is_reported():
         assert g.status() == 0
     finally:
         g.close()
+
+
+def test_prefetch_into_the_callers_buffer_joins():
+    """A prefetch told the joining call's slot-map buffer writes it directly;
+    a join that passes another buffer gets a copy, and one that passes other
+    selections is checked (with equal contents no status bit, with different
+    contents PREFETCH_MISMATCH); the maps equal a plain resolve's."""
+    torch, hb = _torch(), _hb()
+    cfg = WORKLOADS[4].scaled(B=2, layers=4, L0=5000, steps=2)
+    from tests.gpu_harness import GpuInstance
+    a = GpuInstance(cfg)
+    b = GpuInstance(cfg, hosts=a.hosts)
+    try:
+        dev = "cuda:0"
+        ctx = torch.full((cfg.B,), cfg.L0, dtype=torch.int32, device=dev)
+        _load_windows(a, ctx)
+        _load_windows(b, ctx)
+        sel = torch.from_numpy(np.stack([np.random.default_rng(7 + bb).choice(
+            cfg.L0 - 100, cfg.k, replace=False) for bb in range(cfg.B)]).astype(np.int32)).to(dev)
+        sel_same = sel.clone()              # another buffer, same contents
+        other = sel.flip(1).contiguous()    # another buffer, other contents
+        out = torch.full((cfg.layers, cfg.B, cfg.k), -7, dtype=torch.int32, device=dev)
+        ref = torch.full_like(out, -9)
+        side = torch.cuda.Stream()
+        s = a.stream
+        # layer 1: same buffers -> event wait only
+        hb.hisparse_prefetch(a.h, s, side.cuda_stream, sel.data_ptr(), ctx.data_ptr(), 1,
+                             out[1].data_ptr())
+        hb.hisparse_resolve(a.h, s, sel.data_ptr(), ctx.data_ptr(), 1, out[1].data_ptr())
+        # layer 2: written to a spare buffer, joined into out[2] -> copied
+        spare = torch.full_like(out[2], -5)
+        hb.hisparse_prefetch(a.h, s, side.cuda_stream, sel.data_ptr(), ctx.data_ptr(), 2,
+                             spare.data_ptr())
+        hb.hisparse_resolve(a.h, s, sel.data_ptr(), ctx.data_ptr(), 2, out[2].data_ptr())
+        # layer 3: same out, another selection buffer with the same contents
+        hb.hisparse_prefetch(a.h, s, side.cuda_stream, sel.data_ptr(), ctx.data_ptr(), 3,
+                             out[3].data_ptr())
+        hb.hisparse_resolve(a.h, s, sel_same.data_ptr(), ctx.data_ptr(), 3, out[3].data_ptr())
+        hb.hisparse_resolve(a.h, s, sel.data_ptr(), ctx.data_ptr(), 0, out[0].data_ptr())
+        torch.cuda.synchronize()
+        assert a.status() == 0
+        for l in range(cfg.layers):
+            hb.hisparse_resolve(b.h, b.stream, sel.data_ptr(), ctx.data_ptr(), l, ref[l].data_ptr())
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert torch.equal(spare, ref[2])
+        _assert_same_state(a, b, cfg)
+        # a join with other contents in another buffer is reported
+        hb.hisparse_prefetch(a.h, s, side.cuda_stream, sel.data_ptr(), ctx.data_ptr(), 1,
+                             out[1].data_ptr())
+        hb.hisparse_resolve(a.h, s, other.data_ptr(), ctx.data_ptr(), 1, out[1].data_ptr())
+        torch.cuda.synchronize()
+        assert a.status(clear=True) & hb.HISPARSE_STATUS_PREFETCH_MISMATCH
+        assert a.status() == 0
+    finally:
+        b.close()
+        a.close()
 
 
 def test_no_io_equals_io_metadata_and_reads_nothing():
