@@ -352,12 +352,13 @@ def calibration_copy():
 
 
 KERNEL_NAMES = ("mla_decode_kernel", "mla_combine_kernel", "topk_hist_kernel", "topk_filter_kernel",
-                "topk_finish_kernel", "resolve_kernel", "fetch_kernel")
+                "topk_finish_kernel", "resolve_kernel", "fetch_stream_kernel", "fetch_kernel",
+                "prefetch_join_kernel")
 
 
 def short_kernel_name(name):
     for key in ("mla_decode_kernel", "mla_combine_kernel", "topk_hist_kernel", "topk_filter_kernel",
-                "topk_finish_kernel", "resolve_kernel", "fetch_kernel",
+                "topk_finish_kernel", "resolve_kernel", "fetch_stream_kernel", "fetch_kernel",
                 "probe_host_read_kernel", "init_kernel",
                 "load_window_kernel", "append_kernel", "prefetch_join_kernel"):
         if key in name:
@@ -1096,7 +1097,9 @@ def main():
         avg_miss = tot_miss / max(1, n_calls * cfg.B)
         avg_hit = tot_hit / max(1, n_calls * cfg.B)
         meta_bytes = cfg.B * (12 * cfg.k + 16 * cfg.C + 4 * (avg_hit + avg_miss) + 24 * avg_miss + 64)
-        dominant = "resolve_kernel" if fused else "fetch_kernel"
+        # the library's split fetch: sliced per stream below 8 streams per call
+        dominant = ("resolve_kernel" if fused else
+                    "fetch_stream_kernel" if cfg.B < 8 else "fetch_kernel")
         alg_traffic = 2 * fetch_bytes_per_launch + (meta_bytes if fused else 0)
         traffic = committed_traffic(dominant, cfg.label, "fused" if fused else "split")
         # counters are reported only when taken over the same K steps (from a
