@@ -55,12 +55,13 @@ inline hisparse_meta_layout meta_layout(const hisparse_config& c) {
   return m;
 }
 
-// Launch shape of the resolve kernel: `items` entries per thread (a power of
-// two) and `threads` threads cover max(k, C) entries.
+// Launch shape of the resolve kernel: `threads` threads with `items` LRU-order
+// entries each cover max(k, C); `sel_items` selections each cover k.
 struct ResolveShape {
   int items;
   int threads;
   size_t lds_bytes;
+  int sel_items;
 };
 
 // Everything a kernel needs to address one layer's streams.

@@ -15,9 +15,10 @@
 //   * one workgroup per stream (request, layer); the work is latency-bound
 //     (two dependent HBM round trips: selections, then the position->slot
 //     gathers), so everything else stays in LDS and registers;
-//   * each thread owns `IPT` selections and `IPT` LRU-order entries, strided
-//     by the workgroup size, so every global load is coalesced except the
-//     position->slot gathers;
+//   * each thread owns `IPS` selections and `IPO` LRU-order entries, strided
+//     by the workgroup size (sized for the C order entries; the k <= C
+//     selections take as few items per thread as cover them), so every
+//     global load is coalesced except the position->slot gathers;
 //   * three ordered compactions (misses by selection index, unreferenced
 //     slots by LRU order, referenced slots by slot number) use 64-lane
 //     ballots plus per-(round, wave) counts in LDS, one barrier each;
@@ -170,7 +171,7 @@ __device__ __forceinline__ bool test_bit(const uint32_t* bm, int s) {
 // the union written in first-occurrence order.  The first entries leave
 // their slot in LDS, and after barrier 3 every repeat is served that slot.
 // ---------------------------------------------------------------------------
-template <int IPT, bool kAppend>
+template <int IPS, int IPO, bool kAppend>
 __global__ void __launch_bounds__(kMaxThreads)
     resolve_kernel(StreamView v, int layer, const int32_t* __restrict__ sel_all,
                    const int32_t* __restrict__ ctx_len, int32_t* __restrict__ out_all,
@@ -201,8 +202,8 @@ __global__ void __launch_bounds__(kMaxThreads)
   int* missp = s2p + C;
   int* missi = missp + k;
   int* cntA = missi + k;
-  int* cntB = cntA + IPT * W;
-  int* misc = cntB + IPT * W;  // 0 error bits, 1 pad, 2 res, 3 hit, 4 evictions
+  int* cntB = cntA + IPS * W;
+  int* misc = cntB + IPO * W;  // 0 error bits, 1 pad, 2 res, 3 hit, 4 evictions
   const int H = multi ? (2 << (31 - __clz(2 * ke - 1)))   // power of two >= 2 ke
                       : debug ? (2 << (31 - __clz(k)))    // power of two > k
                               : 0;
@@ -232,16 +233,16 @@ __global__ void __launch_bounds__(kMaxThreads)
   }
 
   // ---- Phase A: independent loads; clear LDS ------------------------------
-  int32_t p[IPT], o[IPT], q2[IPT], slot[IPT];
-  int cls[IPT];
+  int32_t p[IPS], slot[IPS], o[IPO], q2[IPO];
+  int cls[IPS];
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPS; ++r) {
     const int i = r * BD + tid;
     p[r] = (i < ke) ? sel[i] : -1;
     cls[r] = (i < ke) ? kPad : kNone;
   }
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPO; ++r) {
     const int x = r * BD + tid;
     o[r] = (x < C) ? st.order[x] : 0;
     q2[r] = (x < C) ? st.slot2pos[x] : -1;
@@ -265,7 +266,7 @@ __global__ void __launch_bounds__(kMaxThreads)
   // ---- classify; the position->slot gathers -------------------------------
   uint32_t bad = ctx_ok ? 0u : (uint32_t)HISPARSE_STATUS_CTX_RANGE;
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPS; ++r) {
     slot[r] = -1;
     if (cls[r] == kNone) continue;
     const int32_t q = p[r];
@@ -283,16 +284,16 @@ __global__ void __launch_bounds__(kMaxThreads)
     }
   }
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPO; ++r) {
     const int x = r * BD + tid;
     if (x < C) s2p[x] = q2[r];
   }
-  int hs[IPT];  // several queries: the entry's hash cell, -1 if none
+  int hs[IPS];  // several queries: the entry's hash cell, -1 if none
   if (multi) {
     // Open addressing with linear probing; H >= 2 ke > number of distinct
     // positions, so every probe sequence ends at its key or a free cell.
 #pragma unroll
-    for (int r = 0; r < IPT; ++r) {
+    for (int r = 0; r < IPS; ++r) {
       hs[r] = -1;
       if (cls[r] != kRes && cls[r] != kMiss) continue;
       uint32_t h = ((uint32_t)p[r] * 2654435761u) & (uint32_t)(H - 1);
@@ -306,11 +307,11 @@ __global__ void __launch_bounds__(kMaxThreads)
     }
     lds_barrier();  // D: the first entry of every position is known
 #pragma unroll
-    for (int r = 0; r < IPT; ++r)
+    for (int r = 0; r < IPS; ++r)
       if (hs[r] >= 0 && first[hs[r]] != r * BD + tid) cls[r] = kRepeat;
   } else if (debug) {  // repeated positions: LDS open-addressing set of size H
 #pragma unroll
-    for (int r = 0; r < IPT; ++r) {
+    for (int r = 0; r < IPS; ++r) {
       if (cls[r] == kNone || p[r] < 0) continue;
       uint32_t h = ((uint32_t)p[r] * 2654435761u) & (uint32_t)(H - 1);
       while (true) {
@@ -324,11 +325,12 @@ __global__ void __launch_bounds__(kMaxThreads)
       }
     }
   }
-  bool flag[IPT];
-  int pre[IPT], off[IPT];
+  // compaction flags, in-wave ranks and offsets: selections (s), LRU order (o)
+  bool fs[IPS], fo[IPO];
+  int ps[IPS], os_[IPS], po[IPO], oo[IPO];
   int npad = 0, nres = 0, nhit = 0;
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPS; ++r) {
     if (cls[r] == kMiss && slot[r] >= 0) {
       cls[r] = kHit;
       atomicOr(&bitmap[slot[r] >> 5], 1u << (slot[r] & 31));
@@ -336,9 +338,9 @@ __global__ void __launch_bounds__(kMaxThreads)
     npad += __popcll(__ballot(cls[r] == kPad || cls[r] == kRepeat));
     nres += __popcll(__ballot(cls[r] == kRes));
     nhit += __popcll(__ballot(cls[r] == kHit));
-    flag[r] = cls[r] == kMiss;
+    fs[r] = cls[r] == kMiss;
   }
-  ballot_counts<IPT>(flag, cntA, W, wave, lane, pre);
+  ballot_counts<IPS>(fs, cntA, W, wave, lane, ps);
   if (bad) atomicOr((uint32_t*)&misc[0], bad);
   if (lane == 0) {
     if (npad) atomicAdd(&misc[1], npad);
@@ -353,7 +355,7 @@ __global__ void __launch_bounds__(kMaxThreads)
     if (err & (HISPARSE_STATUS_SEL_RANGE | HISPARSE_STATUS_CTX_RANGE))
       err &= ~(uint32_t)HISPARSE_STATUS_SEL_DUP;
 #pragma unroll
-    for (int r = 0; r < IPT; ++r) {
+    for (int r = 0; r < IPS; ++r) {
       const int i = r * BD + tid;
       if (i < ke) {
         out[i] = -1;
@@ -370,12 +372,12 @@ __global__ void __launch_bounds__(kMaxThreads)
   const int n_hit = misc[3];
 
   // ---- serve padding, resident rows and hits; stage the misses -------------
-  const int M = scan_offsets<IPT>([&](int e) { return cntA[e]; }, W, wave, lane, off);
+  const int M = scan_offsets<IPS>([&](int e) { return cntA[e]; }, W, wave, lane, os_);
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPS; ++r) {
     const int i = r * BD + tid;
     if (cls[r] == kMiss) {  // j-th miss in ascending selection index
-      const int j = off[r] + pre[r];
+      const int j = os_[r] + ps[r];
       missp[j] = p[r];
       missi[j] = i;
     } else if (cls[r] == kPad) {
@@ -391,18 +393,18 @@ __global__ void __launch_bounds__(kMaxThreads)
     if (sel_copy && cls[r] != kNone) sel_copy[(int64_t)b * k + i] = p[r];
   }
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPO; ++r) {
     const int x = r * BD + tid;
-    flag[r] = (x < C) && !test_bit(bitmap, o[r]);  // unreferenced, in LRU order
+    fo[r] = (x < C) && !test_bit(bitmap, o[r]);  // unreferenced, in LRU order
   }
-  ballot_counts<IPT>(flag, cntB, W, wave, lane, pre);
+  ballot_counts<IPO>(fo, cntB, W, wave, lane, po);
   lds_barrier();  // 2: misses staged, unreferenced-slot counts
 
   // ---- fused fetch, first chunks: the missing positions are known, their --
   // slots are not yet.  Start the first kPre 16-byte host reads per thread
   // now, so the host link is busy while the victims are chosen and the LRU
   // order is rebuilt; they are stored once the slots are known.
-  constexpr int kPre = IPT <= 8 ? 4 : 0;
+  constexpr int kPre = IPO <= 8 ? 4 : 0;
   const bool fuse = v.fuse_fetch && !(v.flags & HISPARSE_NO_IO);
   const uint32_t cpr = (uint32_t)(v.row_bytes >> 4);
   const uint32_t total = fuse ? (uint32_t)M * cpr : 0u;
@@ -422,12 +424,12 @@ __global__ void __launch_bounds__(kMaxThreads)
 
   // ---- victims = first M unreferenced slots in LRU order; the j-th miss ----
   // takes the j-th victim.  The victim's owner thread applies the whole miss.
-  scan_offsets<IPT>([&](int e) { return cntB[e]; }, W, wave, lane, off);
+  scan_offsets<IPO>([&](int e) { return cntB[e]; }, W, wave, lane, oo);
   int nev = 0;
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
-    if (!flag[r]) continue;
-    const int u = off[r] + pre[r];
+  for (int r = 0; r < IPO; ++r) {
+    if (!fo[r]) continue;
+    const int u = oo[r] + po[r];
     const int s = o[r];
     if (u < M) {
       const int pos = missp[u];
@@ -457,29 +459,29 @@ __global__ void __launch_bounds__(kMaxThreads)
   // e = r*W + w covers slots [64e, 64e + 64) = bitmap words 2e and 2e + 1.
   const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
+  for (int r = 0; r < IPO; ++r) {
     const int x = r * BD + tid;
-    flag[r] = (x < C) && test_bit(bitmap, x);
-    pre[r] = __popcll(__ballot(flag[r]) & lt);
+    fo[r] = (x < C) && test_bit(bitmap, x);
+    po[r] = __popcll(__ballot(fo[r]) & lt);
   }
-  scan_offsets<IPT>(
+  scan_offsets<IPO>(
       [&](int e) {
         const int w0 = 2 * e;
         return (w0 < nbm ? __popc(bitmap[w0]) : 0) + (w0 + 1 < nbm ? __popc(bitmap[w0 + 1]) : 0);
       },
-      W, wave, lane, off);
+      W, wave, lane, oo);
   const int base = C - (n_hit + M);
 #pragma unroll
-  for (int r = 0; r < IPT; ++r) {
-    if (!flag[r]) continue;
+  for (int r = 0; r < IPO; ++r) {
+    if (!fo[r]) continue;
     const int x = r * BD + tid;
-    st.order[base + off[r] + pre[r]] = x;
+    st.order[base + oo[r] + po[r]] = x;
     st.last_use[x] = t;
     st.slot2pos[x] = s2p[x];
   }
   if (multi) {  // repeats: the slot of the position's first entry
 #pragma unroll
-    for (int r = 0; r < IPT; ++r)
+    for (int r = 0; r < IPS; ++r)
       if (cls[r] == kRepeat) out[r * BD + tid] = eslot[first[hs[r]]];
   }
 
@@ -834,10 +836,12 @@ hipError_t launch_timed(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t
 }  // namespace
 
 ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries) {
-  // Fewest items per thread that fit 1024 threads; then the fewest 64-lane
-  // waves that cover max(k, C) with that many items each.
+  // Fewest order items per thread that fit 1024 threads; then the fewest
+  // 64-lane waves that cover max(k, C) with that many items each; then the
+  // fewest selection items (1, 2, 4 or the order items) that cover k with
+  // those threads.
   const int n = k > C ? k : C;
-  ResolveShape s{0, 0, 0};
+  ResolveShape s{0, 0, 0, 0};
   static const int kItems[] = {1, 2, 3, 4, 6, 8, 12, 16};
   for (int items : kItems) {
     int threads = (n + items - 1) / items;
@@ -849,8 +853,12 @@ ResolveShape resolve_shape(int k, int C, bool debug_validate, int multi_entries)
     }
   }
   if (s.items == 0) return s;
+  // instantiated selection counts: 1, 2, 4 and the order count itself
+  const int need = (k + s.threads - 1) / s.threads;
+  s.sel_items = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 && s.items >= 4 ? 4 : s.items;
+  if (s.sel_items > s.items) s.sel_items = s.items;
   const int W = s.threads / 64;
-  size_t words = (size_t)((C + 31) / 32) + C + 2 * (size_t)k + 2 * (size_t)s.items * W + 8;
+  size_t words = (size_t)((C + 31) / 32) + C + 2 * (size_t)k + (size_t)(s.items + s.sel_items) * W + 8;
   if (multi_entries > 0)
     words += 2 * (size_t)(2 << (31 - __builtin_clz((unsigned)(2 * multi_entries - 1))));
   else if (debug_validate)
@@ -866,23 +874,40 @@ hipError_t launch_resolve(const StreamView& v, hipStream_t s, int layer, const i
   const ResolveShape sh =
       resolve_shape(v.k, v.C, (v.flags & HISPARSE_DEBUG_VALIDATE) != 0, multi_entries);
   const dim3 grid(v.B), block(sh.threads);
-  switch (sh.items) {
-#define HSP_RESOLVE_CASE(N)                                                                    \
-  case N:                                                                                      \
-    return app_rows ? launch_timed(resolve_kernel<N, true>, grid, block, sh.lds_bytes, s, ev0,  \
-                                   ev1, v, layer, sel, ctx_len, out, sel_copy, multi_entries,   \
-                                   app_rows, app_pos)                                           \
-                    : launch_timed(resolve_kernel<N, false>, grid, block, sh.lds_bytes, s, ev0, \
-                                   ev1, v, layer, sel, ctx_len, out, sel_copy, multi_entries,   \
-                                   app_rows, app_pos);
-    HSP_RESOLVE_CASE(1)
-    HSP_RESOLVE_CASE(2)
-    HSP_RESOLVE_CASE(3)
-    HSP_RESOLVE_CASE(4)
-    HSP_RESOLVE_CASE(6)
-    HSP_RESOLVE_CASE(8)
-    HSP_RESOLVE_CASE(12)
-    HSP_RESOLVE_CASE(16)
+  switch (sh.sel_items * 32 + sh.items) {
+#define HSP_RESOLVE_CASE(S, O)                                                                 \
+  case S * 32 + O:                                                                             \
+    return app_rows ? launch_timed(resolve_kernel<S, O, true>, grid, block, sh.lds_bytes, s,    \
+                                   ev0, ev1, v, layer, sel, ctx_len, out, sel_copy,             \
+                                   multi_entries, app_rows, app_pos)                            \
+                    : launch_timed(resolve_kernel<S, O, false>, grid, block, sh.lds_bytes, s,   \
+                                   ev0, ev1, v, layer, sel, ctx_len, out, sel_copy,             \
+                                   multi_entries, app_rows, app_pos);
+    HSP_RESOLVE_CASE(1, 1)
+    HSP_RESOLVE_CASE(1, 2)
+    HSP_RESOLVE_CASE(2, 2)
+    HSP_RESOLVE_CASE(1, 3)
+    HSP_RESOLVE_CASE(2, 3)
+    HSP_RESOLVE_CASE(3, 3)
+    HSP_RESOLVE_CASE(1, 4)
+    HSP_RESOLVE_CASE(2, 4)
+    HSP_RESOLVE_CASE(4, 4)
+    HSP_RESOLVE_CASE(1, 6)
+    HSP_RESOLVE_CASE(2, 6)
+    HSP_RESOLVE_CASE(4, 6)
+    HSP_RESOLVE_CASE(1, 8)
+    HSP_RESOLVE_CASE(2, 8)
+    HSP_RESOLVE_CASE(4, 8)
+    HSP_RESOLVE_CASE(1, 12)
+    HSP_RESOLVE_CASE(2, 12)
+    HSP_RESOLVE_CASE(4, 12)
+    HSP_RESOLVE_CASE(1, 16)
+    HSP_RESOLVE_CASE(2, 16)
+    HSP_RESOLVE_CASE(4, 16)
+    HSP_RESOLVE_CASE(6, 6)
+    HSP_RESOLVE_CASE(8, 8)
+    HSP_RESOLVE_CASE(12, 12)
+    HSP_RESOLVE_CASE(16, 16)
 #undef HSP_RESOLVE_CASE
     default:
       return hipErrorInvalidValue;
