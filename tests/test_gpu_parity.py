@@ -213,3 +213,28 @@ def test_long_run_many_cache_turnovers():
         assert int(hdr[0]) == cfg.steps
     finally:
         run.close()
+
+
+# One (k, C) per instantiation of the resolve kernel: (selection items, order
+# items) per thread, from the smallest cache that yields the pair (the largest
+# k there), so both sides run their full item counts.
+KERNEL_SHAPES = {
+    (1, 1): (1, 1), (1, 2): (576, 1025), (1, 3): (704, 2049), (1, 4): (832, 3073),
+    (1, 6): (704, 4097), (1, 8): (832, 6145), (1, 12): (704, 8193), (1, 16): (832, 12289),
+    (2, 2): (1025, 1025), (2, 3): (1408, 2049), (2, 4): (1664, 3073), (2, 6): (1408, 4097),
+    (2, 8): (1664, 6145), (2, 12): (1408, 8193), (2, 16): (1664, 12289), (3, 3): (2049, 2049),
+    (4, 4): (3073, 3073), (4, 6): (2816, 4097), (4, 8): (3328, 6145), (4, 12): (2816, 8193),
+    (4, 16): (3328, 12289), (6, 6): (4096, 4097), (8, 8): (4096, 6145), (12, 12): (4096, 8193),
+    (16, 16): (4096, 12289),
+}
+
+
+@pytest.mark.parametrize("pair", sorted(KERNEL_SHAPES), ids=lambda p: f"sel{p[0]}_ord{p[1]}")
+def test_every_resolve_kernel_instantiation(pair):
+    """Every (selection, LRU-order) items-per-thread instantiation of the
+    resolve kernel, against the oracle for three steps (one request, half
+    the selections carried over, so later steps hit, miss and evict)."""
+    k, C = KERNEL_SHAPES[pair]
+    cfg = WORKLOADS[1].scaled(L0=2 * C + 1000, C=C, k=k, steps=3, carry_pct=50)
+    print(f"[shape] items {pair}: k={k} C={C}", flush=True)
+    _run_lockstep(cfg)
