@@ -154,9 +154,9 @@ __device__ __forceinline__ bool test_bit(const uint32_t* bm, int s) {
 // row leaves the stream untouched.
 //
 // Fused append (`app_rows` not NULL; the host calls it only with a resident
-// window, R >= 1): before resolving, the request's new row goes to host
-// history row pos = app_pos[b] and to ring slot C + pos mod R, as the
-// separate append does.  Nothing in the resolution reads either: pos is the
+// window, R >= 1): the request's new row goes to host history row
+// pos = app_pos[b] and to ring slot C + pos mod R, as the separate append
+// does.  Nothing in the resolution reads either: pos is the
 // last position of the context, hence resident (never looked up, never
 // fetched), and misses are fetched into LRU slots only; so the stores run
 // alongside the resolution and the launch's end orders them before any later
@@ -211,27 +211,6 @@ __global__ void __launch_bounds__(kMaxThreads)
   int* first = hash + (multi ? H : 0);
   int* eslot = hash;
 
-  // ---- fused append (see above): host row and ring slot of the new position
-  // (a separate instantiation, so that the plain resolve carries none of it)
-  if (kAppend && R > 0) {
-    const int32_t pos = app_pos[b];
-    if (pos >= v.l_cap) {
-      if (tid == 0) atomicOr(status_word(v), HISPARSE_STATUS_CTX_RANGE);
-    } else if (pos >= 0) {
-      const int cpr = v.row_bytes >> 4;
-      const u32x4* src = reinterpret_cast<const u32x4*>(app_rows + (int64_t)b * v.row_bytes);
-      auto hrow = global_ptr(
-          reinterpret_cast<u32x4*>(v.host[layer * v.B + b] + (int64_t)pos * v.row_bytes));
-      auto ring = global_ptr(reinterpret_cast<u32x4*>(
-          v.cache + ((int64_t)(layer * v.B + b) * (C + R) + C + pos % R) * v.row_bytes));
-      for (int c = tid; c < cpr; c += BD) {
-        const u32x4 val = src[c];
-        hrow[c] = val;
-        ring[c] = val;
-      }
-    }
-  }
-
   // ---- Phase A: independent loads; clear LDS ------------------------------
   int32_t p[IPS], slot[IPS], o[IPO], q2[IPO];
   int cls[IPS];
@@ -261,6 +240,29 @@ __global__ void __launch_bounds__(kMaxThreads)
   if (multi)
     for (int w = tid; w < H; w += BD) first[w] = 0x7fffffff;
   if (tid < 8) misc[tid] = 0;
+
+  // ---- fused append (see above): host row and ring slot of the new position
+  // (a separate instantiation, so that the plain resolve carries none of it).
+  // Issued after the resolution's own loads, so that its two round trips
+  // (position, then row) overlap them instead of delaying them.
+  if (kAppend && R > 0) {
+    const int32_t pos = app_pos[b];
+    if (pos >= v.l_cap) {
+      if (tid == 0) atomicOr(status_word(v), HISPARSE_STATUS_CTX_RANGE);
+    } else if (pos >= 0) {
+      const int cpr = v.row_bytes >> 4;
+      const u32x4* src = reinterpret_cast<const u32x4*>(app_rows + (int64_t)b * v.row_bytes);
+      auto hrow = global_ptr(
+          reinterpret_cast<u32x4*>(v.host[layer * v.B + b] + (int64_t)pos * v.row_bytes));
+      auto ring = global_ptr(reinterpret_cast<u32x4*>(
+          v.cache + ((int64_t)(layer * v.B + b) * (C + R) + C + pos % R) * v.row_bytes));
+      for (int c = tid; c < cpr; c += BD) {
+        const u32x4 val = src[c];
+        hrow[c] = val;
+        ring[c] = val;
+      }
+    }
+  }
   lds_barrier();  // Z: LDS cleared (global loads stay in flight)
 
   // ---- classify; the position->slot gathers -------------------------------
