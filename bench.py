@@ -79,9 +79,10 @@ def parse_args():
                          "with a fixed-duration stand-in for each layer's compute")
     ap.add_argument("--layer-compute-us", type=float, default=312.5,
                     help="stand-in compute per layer for --prefetch-study (20 ms / 64 layers)")
-    ap.add_argument("--layer-compute", choices=("busy", "attention"), default="busy",
-                    help="--prefetch-study per-layer compute: the calibrated busy kernel, or the "
-                         "sparse MLA decode attention over the layer's slot map (--heads)")
+    ap.add_argument("--layer-compute", choices=("busy", "attention", "none"), default="busy",
+                    help="--prefetch-study per-layer compute: the calibrated busy kernel, the "
+                         "sparse MLA decode attention over the layer's slot map (--heads), or "
+                         "none (the schedules' own overlap)")
     ap.add_argument("--mla-attention", action="store_true",
                     help="time sparse MLA decode attention over the slot map (one layer)")
     ap.add_argument("--heads", type=int, default=16, help="query heads for --mla-attention")
@@ -504,12 +505,16 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
     """Exact layer-wise prefetch on a shared-selection workload.
 
     Per layer a stand-in compute kernel (torch's fixed-cycle busy kernel,
-    calibrated to `compute_us`) runs on the main stream.  Three schedules,
-    each captured as one HIP graph of K steps and replayed from a cold cache:
-      serial:   resolve(l); compute(l)                       for every layer
-      prefetch: resolve(0); then per layer prefetch(l+1) on a side stream,
-                compute(l), resolve(l+1) joins it
-      no-IO:    the serial schedule with copies suppressed
+    calibrated to `compute_us`; the sparse attention; or nothing) runs on the
+    main stream.  Four schedules, each captured as one HIP graph of K steps
+    and replayed after the warm-up steps:
+      serial:    resolve(l); compute(l)                       for every layer
+      prefetch:  resolve(0); then per layer prefetch(l+1) on a side stream,
+                 compute(l), resolve(l+1) joins it
+      two ahead: resolve(0), prefetch(1); then per layer prefetch(l+2) on the
+                 other of two side streams, compute(l), resolve(l+1) joins:
+                 two layers' launches in flight at once
+      no-IO:     the serial schedule with copies suppressed
     hidden = 1 - (T_prefetch - T_noIO) / (T_serial - T_noIO).
     """
     torch, hb, cfg = setup.torch, setup.hb, setup.cfg
@@ -538,16 +543,16 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
             hb.hisparse_sparse_mla_decode(inst.h, ms, l, qs[l].data_ptr(), setup.out[l].data_ptr(),
                                           heads, 1.0 / np.sqrt(576.0), attn[id(inst)].data_ptr(),
                                           a_out.data_ptr(), a_lse.data_ptr())
-        else:
+        elif compute == "busy":
             torch.cuda._sleep(cyc)
 
-    def serial(inst, s, ms, ss):
+    def serial(inst, s, ms, ss, ss2):
         for l in range(cfg.layers):
             hb.hisparse_resolve(inst.h, ms, setup.sel[s, l].data_ptr(), setup.ctx[s].data_ptr(), l,
                                 setup.out[l].data_ptr())
             layer_compute(inst, l, ms)
 
-    def prefetched(inst, s, ms, ss):
+    def prefetched(inst, s, ms, ss, ss2):
         hb.hisparse_resolve(inst.h, ms, setup.sel[s, 0].data_ptr(), setup.ctx[s].data_ptr(), 0,
                             setup.out[0].data_ptr())
         for l in range(cfg.layers):
@@ -559,15 +564,31 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
                 hb.hisparse_resolve(inst.h, ms, setup.sel[s, l + 1].data_ptr(),
                                     setup.ctx[s].data_ptr(), l + 1, setup.out[l + 1].data_ptr())
 
+    def two_ahead(inst, s, ms, ss, ss2):
+        sides = (ss, ss2)
+        hb.hisparse_resolve(inst.h, ms, setup.sel[s, 0].data_ptr(), setup.ctx[s].data_ptr(), 0,
+                            setup.out[0].data_ptr())
+        if cfg.layers > 1:
+            hb.hisparse_prefetch(inst.h, ms, sides[1], setup.sel[s, 1].data_ptr(),
+                                 setup.ctx[s].data_ptr(), 1, setup.out[1].data_ptr())
+        for l in range(cfg.layers):
+            if l + 2 < cfg.layers:
+                hb.hisparse_prefetch(inst.h, ms, sides[l % 2], setup.sel[s, l + 2].data_ptr(),
+                                     setup.ctx[s].data_ptr(), l + 2, setup.out[l + 2].data_ptr())
+            layer_compute(inst, l, ms)
+            if l + 1 < cfg.layers:
+                hb.hisparse_resolve(inst.h, ms, setup.sel[s, l + 1].data_ptr(),
+                                    setup.ctx[s].data_ptr(), l + 1, setup.out[l + 1].data_ptr())
+
     W = setup.W
 
     def timed(inst, schedule):
-        main, side = torch.cuda.Stream(), torch.cuda.Stream()
+        main, side, side2 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(main):
             with torch.cuda.graph(g, stream=main):
                 for s in range(W, W + K):
-                    schedule(inst, s, main.cuda_stream, side.cuda_stream)
+                    schedule(inst, s, main.cuda_stream, side.cuda_stream, side2.cuda_stream)
         torch.cuda.synchronize()
         best = None
         for _ in range(2):
@@ -582,18 +603,28 @@ def prefetch_study(setup, K, compute_us, compute="busy", heads=16):
 
     t_serial = timed(setup.io, serial)
     t_pref = timed(setup.io, prefetched)
+    t_two = timed(setup.io, two_ahead)
     t_noio = timed(setup.noio, serial)
-    hidden = 1.0 - (t_pref - t_noio) / (t_serial - t_noio) if t_serial > t_noio else None
+    t_noio_two = timed(setup.noio, two_ahead)
+
+    def hidden_of(t):
+        return round(1.0 - (t - t_noio) / (t_serial - t_noio), 4) if t_serial > t_noio else None
+
     return {"metric": "layer-wise prefetch: hidden fraction of the miss overhead",
-            "value": round(hidden, 4) if hidden is not None else None, "unit": "fraction",
+            "value": hidden_of(t_pref), "unit": "fraction",
+            "value_two_ahead": hidden_of(t_two),
             "workload": cfg.name, "steps": K, "layers": cfg.layers,
             "layer_compute": (f"sparse MLA attention, {heads} heads" if compute == "attention"
+                              else "none" if compute == "none"
                               else f"busy kernel, {round(cyc * us_per_cycle, 2)} us"),
             "ms_per_step": {"serial": round(t_serial / K * 1e3, 4),
                             "prefetch": round(t_pref / K * 1e3, 4),
-                            "no_io": round(t_noio / K * 1e3, 4)},
+                            "two_ahead": round(t_two / K * 1e3, 4),
+                            "no_io": round(t_noio / K * 1e3, 4),
+                            "no_io_two_ahead": round(t_noio_two / K * 1e3, 4)},
             "miss_overhead_us_per_step": {"serial": round((t_serial - t_noio) / K * 1e6, 1),
-                                          "prefetch": round((t_pref - t_noio) / K * 1e6, 1)},
+                                          "prefetch": round((t_pref - t_noio) / K * 1e6, 1),
+                                          "two_ahead": round((t_two - t_noio) / K * 1e6, 1)},
             "mode": f"one HIP graph per schedule of steps {W} .. {W + K - 1}, best of 2 replays "
                     f"after the {W} warm-up steps"}
 
@@ -1306,7 +1337,8 @@ def main():
                 result["prefetch"] = {
                     "stand_in_compute": prefetch_study(setup, K, args.layer_compute_us, "busy"),
                     "attention_compute": prefetch_study(setup, K, 0.0, "attention",
-                                                        args.heads)}
+                                                        args.heads),
+                    "no_compute": prefetch_study(setup, K, 0.0, "none")}
                 log("prefetch study: hidden fraction {} (stand-in compute), {} (attention)".format(
                     result["prefetch"]["stand_in_compute"]["value"],
                     result["prefetch"]["attention_compute"]["value"]))

@@ -116,6 +116,25 @@ class LockstepRun:
             hb.hisparse_resolve(h, main, sel[l + 1].data_ptr(), ctx.data_ptr(), l + 1,
                                 out[l + 1].data_ptr())
 
+    def prefetch_ahead_step(self, s: int, main: int, sides, sel=None, ctx=None):
+        """Step s with two layers in flight: layer 0 resolved on `main`, layer 1
+        prefetched; then before each layer l is joined, layer l+1 is prefetched
+        on the other side stream, so its launch runs while layer l's prefetch
+        still does.  Every prefetch writes the layer's slot-map buffer itself."""
+        sel = self.sel_dev[s] if sel is None else sel
+        ctx = self.ctx_dev[s] if ctx is None else ctx
+        out = self.out_dev
+        h, L = self.gpu.h, self.cfg.layers
+        hb.hisparse_resolve(h, main, sel[0].data_ptr(), ctx.data_ptr(), 0, out[0].data_ptr())
+        if L > 1:
+            hb.hisparse_prefetch(h, main, sides[1 % 2], sel[1].data_ptr(), ctx.data_ptr(), 1,
+                                 out[1].data_ptr())
+        for l in range(1, L):
+            if l + 1 < L:
+                hb.hisparse_prefetch(h, main, sides[(l + 1) % 2], sel[l + 1].data_ptr(),
+                                     ctx.data_ptr(), l + 1, out[l + 1].data_ptr())
+            hb.hisparse_resolve(h, main, sel[l].data_ptr(), ctx.data_ptr(), l, out[l].data_ptr())
+
     def oracle_step(self, s: int):
         return self.oracle.step(s, self.trace, no_io=self.no_io, queries=self.queries)
 

@@ -279,6 +279,46 @@ def test_prefetch_schedule_against_the_oracle(captured, k, direct):
         run.close()
 
 
+@pytest.mark.parametrize("captured", [False, True])
+def test_two_prefetches_in_flight_against_the_oracle(captured):
+    """Two layers resolved at once: each layer l+1 is prefetched on one of
+    two side streams before layer l is joined, so the launches of layers l and
+    l+1 overlap on the GPU (with 8 requests the misses are copied by the
+    resolve launches themselves).  Each layer keeps its own state, so every
+    step must still equal the oracle resolving the layers in order."""
+    torch, hb = _torch(), _hb()
+    from tests.gpu_harness import LockstepRun
+    cfg = WORKLOADS[4].scaled(B=8, layers=5, L0=30000, C=3000, k=1500, steps=8)
+    run = LockstepRun(cfg)
+    try:
+        main, sides = torch.cuda.Stream(), (torch.cuda.Stream(), torch.cuda.Stream())
+        side_ptrs = tuple(x.cuda_stream for x in sides)
+        sel_buf = torch.empty_like(run.sel_dev[0])
+        ctx_buf = torch.empty_like(run.ctx_dev[0])
+        graph = None
+        if captured:
+            graph = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(main):
+                with torch.cuda.graph(graph, stream=main):
+                    run.prefetch_ahead_step(0, main.cuda_stream, side_ptrs, sel=sel_buf, ctx=ctx_buf)
+            torch.cuda.synchronize()
+        for s in range(cfg.steps):
+            if captured:
+                sel_buf.copy_(run.sel_dev[s])
+                ctx_buf.copy_(run.ctx_dev[s])
+                torch.cuda.synchronize()
+                graph.replay()
+            else:
+                torch.cuda.synchronize()
+                run.prefetch_ahead_step(s, main.cuda_stream, side_ptrs)
+            torch.cuda.synchronize()
+            run.compare_step(s, run.oracle_step(s))
+        assert run.gpu.status() == 0
+    finally:
+        run.close()
+
+
 def test_prefetch_over_a_growing_context_against_the_oracle():
     """Shared selections over a context that grows by one row per step: each
     layer's new row goes in through hisparse_append_resolve while the layer
