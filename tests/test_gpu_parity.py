@@ -44,6 +44,10 @@ CASES = {
     # the context grows past the window (58 .. 69 rows, R = 64): the first steps are all
     # resident, then the oldest positions leave the window and are fetched when selected
     "window_boundary_crossing": (3, dict(B=2, layers=1, L0=58, C=64, R=64, k=24, steps=12)),
+    # the largest cache and selection the library accepts (C = 16384, k = 4096)
+    "maximum_cache_and_k": (1, dict(L0=70000, C=16384, k=4096, steps=4)),
+    # more streams per call than the GPU has CUs: the resolve grid runs in several rounds
+    "more_requests_than_cus": (2, dict(B=300, L0=2000, C=96, R=8, k=48, steps=4)),
 }
 
 
@@ -55,7 +59,8 @@ def test_parity_reduced(name):
 
 @pytest.mark.parametrize("mode", ["fused", "split"])
 @pytest.mark.parametrize("name", ["one_request_ragged", "independent_layers_growth", "pages",
-                                  "largest_supported_shape", "many_requests"])
+                                  "largest_supported_shape", "many_requests",
+                                  "maximum_cache_and_k", "more_requests_than_cus"])
 def test_parity_fetch_modes(name, mode, monkeypatch):
     """Both miss-fetch paths (copies by the resolve workgroups themselves, or
     by a separate fan-out kernel: sliced per stream below eight streams per
