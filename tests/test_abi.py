@@ -138,6 +138,22 @@ def test_host_numa_node_of_ordinary_host_memory():
     assert e.value.code == hb.HISPARSE_ERR_INVALID_ARG
 
 
+def test_probe_and_device_node_reject_bad_arguments_before_any_launch():
+    """The link probe validates its arguments on the host (no launch, no GPU
+    needed): NULL buffers, an empty or non-16-byte size, no workgroups and
+    buffers off 16-byte alignment are rejected; so is a NULL node pointer."""
+    lib = hb.library()
+    P, SZ, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    good = 4096   # never dereferenced: every call below fails its checks first
+    for host, dev, nbytes, wgs in ((None, good, 1024, 4), (good, None, 1024, 4),
+                                   (good, good, 0, 4), (good, good, 1000, 4),
+                                   (good, good, 1024, 0), (good + 8, good, 1024, 4),
+                                   (good, good + 4, 1024, 4)):
+        rc = lib.hisparse_probe_host_read(P(None), P(host), P(dev), SZ(nbytes), I32(wgs))
+        assert rc == hb.HISPARSE_ERR_INVALID_ARG, (host, dev, nbytes, wgs, rc)
+    assert lib.hisparse_device_numa_node(None) == hb.HISPARSE_ERR_INVALID_ARG
+
+
 def test_topk_workspace_sizes():
     """Per row: two 4096-bin histograms, a counter block, one bitmap word per
     32 positions rounded up to whole 4096-position chunks, and 8 bytes per

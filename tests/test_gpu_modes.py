@@ -733,3 +733,36 @@ def test_overlapping_output_is_rejected():
         assert g.status() == 0
     finally:
         g.close()
+
+
+@pytest.mark.parametrize("workgroups", [1, 7, 64])
+def test_link_probe_copies_host_bytes_exactly(workgroups):
+    """The link probe (the zero-copy read kernel the benchmark's link peak and
+    counter scaling use) moves pinned host bytes to device memory unchanged,
+    at any grid size, including a size that does not divide evenly."""
+    torch, hb = _torch(), _hb()
+    from hierarchical_kv_cache_hisparse_amd.instance import host_view
+    nbytes = (3 << 20) + 16 * 37
+    ptr = hb.hisparse_host_alloc(nbytes, hb.HISPARSE_HOST_COHERENT)
+    try:
+        view = host_view(ptr, nbytes)
+        view[:] = np.random.default_rng(workgroups).integers(0, 256, nbytes, dtype=np.uint8)
+        dev = torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0")
+        hb.hisparse_probe_host_read(torch.cuda.current_stream().cuda_stream, ptr, dev.data_ptr(),
+                                    nbytes, workgroups)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(dev.cpu().numpy(), view)
+    finally:
+        hb.hisparse_host_free(ptr)
+
+
+def test_device_numa_node_is_a_host_node_or_none():
+    """The GPU's NUMA node is -1 (the device reports none) or a node of this
+    host."""
+    import glob
+    hb = _hb()
+    _torch()
+    node = hb.hisparse_device_numa_node()
+    nodes = {int(p.rsplit("node", 1)[1]) for p in glob.glob("/sys/devices/system/node/node[0-9]*")}
+    assert node == -1 or node in nodes, (node, nodes)
+
